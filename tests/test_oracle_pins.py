@@ -1,0 +1,281 @@
+"""Pins of the CPU oracle against facts other than the oracle itself.
+
+Each test ties one part of oracle/ras.py to a closed form, a hand-derived
+worked example, a library routine in a special case, a brute force on tiny
+inputs, or an invariant the definition forces.  A plausible slip in the oracle
+(a dropped causal mask, a transposed operand, mean instead of max, a wrong
+scale, a wrong tie rule, an off-by-one in the key set) fails at least one.
+"""
+import itertools
+import json
+import math
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+from oracle import ras
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _rand(shape, seed, scale=1.0):
+    return np.random.default_rng(seed).standard_normal(shape) * scale
+
+
+# ---------------------------------------------------------------------------
+# exact conversion of the storage types
+# ---------------------------------------------------------------------------
+
+def test_bf16_conversion_exact_values():
+    bits = np.array([0x3F80, 0xC000, 0x3F81, 0x0001, 0x7F7F, 0x0000, 0x8000], np.uint16)
+    got = ras.bf16_to_f64(bits)
+    want = [1.0, -2.0, 1.0 + 2.0 ** -7, 2.0 ** -133,
+            (2.0 - 2.0 ** -7) * 2.0 ** 127, 0.0, -0.0]
+    assert got.tolist() == want
+
+
+def test_f32_conversion_exact():
+    x = np.array([1.0 / 3.0, 1e-40, -7.25], np.float32)
+    assert ras.to_f64(x, "f32").tolist() == [float(v) for v in x]
+
+
+# ---------------------------------------------------------------------------
+# scoring
+# ---------------------------------------------------------------------------
+
+def test_hand_derived_worked_example():
+    g = json.load(open(os.path.join(GOLDEN, "rational_chunk.json")))
+    q = np.array(g["q_rows"], np.float64)[None, None]          # [1][1][2][2]
+    kc = np.log(np.array(g["k_ctx_log"], np.float64))[None]   # [1][3][2]
+    ki = np.log(np.array(g["k_in_log"], np.float64))[None]    # [1][2][2]
+    P = ras.chunk_probabilities(q[0, 0], kc[0], ki[0], g["scale"])
+    want_p = np.array(g["row_probs_num"], np.float64) / np.array(g["row_probs_den"], np.float64)[:, None]
+    np.testing.assert_allclose(P, want_p, rtol=1e-14, atol=1e-15)
+    S = ras.score_layer([(q, ki)], kc, g["scale"])
+    want = np.array(g["S_num"], np.float64) / np.array(g["S_den"], np.float64)
+    np.testing.assert_allclose(S[0], want, rtol=1e-14)
+
+
+@pytest.mark.parametrize("n_c,n_in,G,H", [(37, 9, 2, 2), (5, 1, 1, 1), (64, 20, 3, 1)])
+def test_zero_queries_closed_form(n_c, n_in, G, H):
+    """Q = 0: every visible key gets 1/(#visible).  Row i sees n_c + i + 1 keys,
+    so every context key's max is 1/(n_c + 1), taken at row 0.  This fixes the
+    key set (the whole context, not only the chunk) and the causal mask over
+    the in-chunk keys (all in-chunk keys visible would give 1/(n_c + n_in))."""
+    d = 8
+    q = np.zeros((H, G, n_in, d))
+    kc = _rand((H, n_c, d), 1)
+    ki = _rand((H, n_in, d), 2)
+    S = ras.score_layer([(q, ki)], kc, 1 / math.sqrt(d))
+    np.testing.assert_allclose(S, 1.0 / (n_c + 1), rtol=1e-14)
+
+
+def test_single_query_row_is_library_softmax():
+    """n_in = 1: S[h] = max_g softmax(scale * q_g . [K_c; k_in_0])[:n_c]."""
+    torch = pytest.importorskip("torch")
+    H, G, n_c, d = 2, 3, 50, 16
+    q = _rand((H, G, 1, d), 3)
+    kc = _rand((H, n_c, d), 4)
+    ki = _rand((H, 1, d), 5)
+    scale = 1 / math.sqrt(d)
+    S = ras.score_layer([(q, ki)], kc, scale)
+    for h in range(H):
+        keys = torch.from_numpy(np.concatenate([kc[h], ki[h]]))
+        lg = torch.from_numpy(q[h, :, 0]) @ keys.T * scale
+        p = torch.softmax(lg, dim=-1)[:, :n_c].max(dim=0).values.numpy()
+        np.testing.assert_allclose(S[h], p, rtol=1e-13, atol=1e-16)
+
+
+def test_rows_are_scipy_softmax_over_visible_prefix():
+    """Each row is the library softmax of the logits of its visible keys: all
+    context keys and in-chunk keys 0..i."""
+    from scipy.special import softmax
+
+    n_c, n_in, d = 23, 7, 8
+    q = _rand((n_in, d), 6)
+    kc = _rand((n_c, d), 7, 2.0)
+    ki = _rand((n_in, d), 8)
+    scale = 0.37
+    P = ras.chunk_probabilities(q, kc, ki, scale)
+    for i in range(n_in):
+        vis = np.concatenate([kc, ki[: i + 1]])
+        want = softmax(vis @ q[i] * scale)
+        np.testing.assert_allclose(P[i, : n_c + i + 1], want, rtol=1e-13, atol=1e-17)
+        assert np.all(P[i, n_c + i + 1:] == 0.0)
+
+
+def test_brute_force_pure_python():
+    """Tiny case by pure-Python loops with math.exp and math.fsum."""
+    H, G, n_c, n_in, d = 2, 2, 5, 3, 4
+    q = _rand((H, G, n_in, d), 9)
+    kc = _rand((H, n_c, d), 10)
+    ki = _rand((H, n_in, d), 11)
+    scale = 0.5
+    S = ras.score_layer([(q, ki)], kc, scale)
+    for h in range(H):
+        best = [0.0] * n_c
+        for g in range(G):
+            for i in range(n_in):
+                keys = [kc[h, j] for j in range(n_c)] + [ki[h, t] for t in range(i + 1)]
+                lg = [scale * math.fsum(float(a) * float(b) for a, b in zip(q[h, g, i], k))
+                      for k in keys]
+                m = max(lg)
+                z = math.fsum(math.exp(x - m) for x in lg)
+                for j in range(n_c):
+                    best[j] = max(best[j], math.exp(lg[j] - m) / z)
+        np.testing.assert_allclose(S[h], best, rtol=1e-12)
+
+
+def test_probability_invariants():
+    n_c, n_in, d = 40, 12, 16
+    q = _rand((n_in, d), 12, 3.0)
+    kc = _rand((n_c, d), 13)
+    ki = _rand((n_in, d), 14)
+    P = ras.chunk_probabilities(q, kc, ki, 1 / 4)
+    np.testing.assert_allclose(P.sum(axis=1), 1.0, atol=1e-12)
+    assert np.all(P >= 0) and np.all(P <= 1)
+    S = ras.score_layer([(q[None, None], ki[None])], kc[None], 1 / 4)
+    assert np.all(S >= 0) and np.all(S <= 1)
+    # S is the column max over rows of the context block, nothing else
+    np.testing.assert_array_equal(S[0], P[:, :n_c].max(axis=0))
+
+
+def test_max_not_mean():
+    """A case where the max and the mean over query rows rank two context keys
+    the other way round; the score must follow the max (blog section 4.3.2;
+    paperhub rebuttal, answer on average aggregation)."""
+    # key A = e0, key B = e1, in-chunk keys = e2; logits are the q entries.
+    kc = np.array([[1.0, 0, 0], [0, 1.0, 0]])
+    n_in = 4
+    ki = np.tile([0, 0, 1.0], (n_in, 1))
+    q = np.array([[5.0, 0, 0]] + [[-5.0, 0.5, 0]] * (n_in - 1))
+    P = ras.chunk_probabilities(q, kc, ki, 1.0)
+    mean = P[:, :2].mean(axis=0)
+    assert mean[1] > mean[0]                         # the mean prefers B
+    S = ras.score_layer([(q[None, None], ki[None])], kc[None], 1.0)[0]
+    assert S[0] > S[1]                               # the max prefers A
+    assert S[0] == pytest.approx(math.exp(5) / (math.exp(5) + 2), rel=1e-14)
+
+
+def test_chunk_merge_is_order_free_and_idempotent():
+    H, G, n_c, d = 2, 2, 30, 8
+    kc = _rand((H, n_c, d), 20)
+    chunks = [(_rand((H, G, n, d), 21 + n), _rand((H, n, d), 40 + n)) for n in (5, 9, 3)]
+    scale = 1 / math.sqrt(d)
+    S = ras.score_layer(chunks, kc, scale)
+    for perm in itertools.permutations(range(3)):
+        S2 = ras.score_layer([chunks[p] for p in perm], kc, scale)
+        np.testing.assert_array_equal(S, S2)
+    S3 = ras.score_layer(chunks + [chunks[1]], kc, scale)
+    np.testing.assert_array_equal(S, S3)
+
+
+def test_group_split_is_max_of_single_heads():
+    H, G, n_c, n_in, d = 1, 3, 25, 6, 8
+    q = _rand((H, G, n_in, d), 30)
+    kc = _rand((H, n_c, d), 31)
+    ki = _rand((H, n_in, d), 32)
+    S = ras.score_layer([(q, ki)], kc, 0.3)
+    parts = [ras.score_layer([(q[:, g:g + 1], ki)], kc, 0.3) for g in range(G)]
+    np.testing.assert_array_equal(S, np.maximum.reduce(parts))
+
+
+def test_scale_enters_as_temperature():
+    """Doubling the scale equals doubling the queries (exactly for powers of 2)."""
+    H, G, n_c, n_in, d = 1, 2, 20, 5, 8
+    q = _rand((H, G, n_in, d), 33)
+    kc = _rand((H, n_c, d), 34)
+    ki = _rand((H, n_in, d), 35)
+    a = ras.score_layer([(q, ki)], kc, 0.5)
+    b = ras.score_layer([(q * 2.0, ki)], kc, 0.25)
+    np.testing.assert_array_equal(a, b)
+    c = ras.score_layer([(q, ki)], kc, 0.25)
+    assert not np.allclose(a, c)
+
+
+# ---------------------------------------------------------------------------
+# selection
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("N,r,K", [(512, 0.3, 154), (2097152, 0.3, 629146),
+                                   (33554432, 0.3, 10066330), (46080000, 0.25, 11520000),
+                                   (65280000, 0.4, 26112000), (10, 0.0, 0), (10, 1.0, 10),
+                                   (7, 0.5, 4)])
+def test_keep_count_values(N, r, K):
+    """K = r * N rounded half up: 0.3 * 512 = 153.6 -> 154, 0.5 * 7 = 3.5 -> 4."""
+    assert ras.keep_count(N, r) == K
+
+
+def _brute_select(S, n_heads, n_c, K):
+    items = sorted(range(len(S)), key=lambda i: (-float(S[i]), i))
+    keep = set(items[:K])
+    mask = [1 if i in keep else 0 for i in range(len(S))]
+    budgets = [sum(mask[h * n_c:(h + 1) * n_c]) for h in range(n_heads)]
+    offs = [0]
+    for b in budgets:
+        offs.append(offs[-1] + b)
+    return mask, offs
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_select_matches_brute_force_with_ties(seed):
+    rng = np.random.default_rng(seed)
+    n_heads, n_c = 4, 9
+    S = rng.integers(0, 5, n_heads * n_c).astype(np.float32) / 8  # many ties
+    for K in (0, 1, 7, 18, 35, 36):
+        mask, offs, tau = ras.select(S, n_heads, n_c, K)
+        bm, bo = _brute_select(S, n_heads, n_c, K)
+        assert mask.tolist() == bm
+        assert offs.tolist() == bo
+        assert int(mask.sum()) == K
+        if 0 < K:
+            assert S[mask == 1].min() >= tau
+            assert tau == sorted(S.tolist(), reverse=True)[K - 1]
+            if K < len(S):
+                assert S[mask == 0].max() <= tau
+        else:
+            assert tau == math.inf
+
+
+def test_select_nonuniform_budgets():
+    """One global threshold gives per-head budgets that follow each head's
+    scores (atlas summary, Measured effects: non-uniform head budgets)."""
+    n_heads, n_c = 3, 10
+    S = np.concatenate([np.full(n_c, 0.9), np.full(n_c, 0.1), np.linspace(0, 1, n_c)])
+    mask, offs, tau = ras.select(S.astype(np.float32), n_heads, n_c, 15)
+    assert np.diff(offs).tolist() == [10, 0, 5]
+
+
+# ---------------------------------------------------------------------------
+# compaction
+# ---------------------------------------------------------------------------
+
+def test_compact_rows_and_index():
+    rng = np.random.default_rng(50)
+    n_heads, n_c, d = 3, 11, 4
+    kc = rng.integers(0, 2 ** 16, (n_heads, n_c, d)).astype(np.uint16)
+    vc = rng.integers(0, 2 ** 16, (n_heads, n_c, d)).astype(np.uint16)
+    S = rng.random(n_heads * n_c).astype(np.float32)
+    mask, offs, _ = ras.select(S, n_heads, n_c, 13)
+    ko, vo, idx = ras.compact(kc, vc, mask, offs)
+    assert ko.shape == (13, d) and idx.shape == (13,)
+    m = mask.reshape(n_heads, n_c)
+    for h in range(n_heads):
+        seg = slice(offs[h], offs[h + 1])
+        js = idx[seg]
+        assert np.all(np.diff(js) > 0)
+        assert set(js.tolist()) == set(np.nonzero(m[h])[0].tolist())
+        assert np.array_equal(ko[seg], kc[h, js]) and np.array_equal(vo[seg], vc[h, js])
+
+
+def test_exact_fractions_for_three_token_case():
+    """Pin with exact rational arithmetic: logits ln(1), ln(2), ln(3) on three
+    context keys and one in-chunk key ln(2), a single query row."""
+    kc = np.log(np.array([[1.0], [2.0], [3.0]]))
+    ki = np.log(np.array([[2.0]]))
+    q = np.array([[[[1.0]]]])
+    S = ras.score_layer([(q, ki[None])], kc[None], 1.0)[0]
+    want = [Fraction(1, 8), Fraction(2, 8), Fraction(3, 8)]
+    np.testing.assert_allclose(S, [float(w) for w in want], rtol=1e-14)
