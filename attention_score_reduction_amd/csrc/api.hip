@@ -1,0 +1,213 @@
+// libkvz C ABI: argument validation, workspace sizing, launch dispatch and
+// the optional kernel timer.  Every entry point validates all arguments
+// before it launches anything; see include/kvz.h for the contract.
+#include <math.h>
+#include <string.h>
+
+#include <string>
+#include <vector>
+
+#include "common.h"
+
+namespace kvz {
+
+// ---------------------------------------------------------------------------
+// kernel timer
+// ---------------------------------------------------------------------------
+namespace {
+struct ProfRec {
+  std::string name;
+  hipEvent_t a, b;
+};
+struct Prof {
+  bool on = false;
+  int max_launches = 0;
+  std::vector<hipEvent_t> pool;
+  std::vector<ProfRec> recs;
+  int pending = -1;
+};
+Prof& prof() {
+  static Prof p;
+  return p;
+}
+}  // namespace
+
+void prof_before(const char* name, hipStream_t s) {
+  Prof& p = prof();
+  p.pending = -1;
+  if (!p.on || (int)p.recs.size() >= p.max_launches) return;
+  const size_t k = p.recs.size();
+  ProfRec r{name, p.pool[2 * k], p.pool[2 * k + 1]};
+  if (hipEventRecord(r.a, s) != hipSuccess) return;
+  p.recs.push_back(r);
+  p.pending = (int)k;
+}
+
+void prof_after(hipStream_t s) {
+  Prof& p = prof();
+  if (p.pending < 0) return;
+  hipEventRecord(p.recs[p.pending].b, s);
+  p.pending = -1;
+}
+
+}  // namespace kvz
+
+using namespace kvz;
+
+namespace {
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool head_dim_ok(int d) { return d == 64 || d == 128 || d == 256; }
+hipError_t clear_error() { return hipGetLastError(); }
+
+}  // namespace
+
+extern "C" {
+
+const char* kvz_status_string(kvz_status s) {
+  switch (s) {
+    case KVZ_OK: return "ok";
+    case KVZ_ERR_INVALID_ARG: return "invalid argument";
+    case KVZ_ERR_UNSUPPORTED: return "unsupported head_dim or dtype";
+    case KVZ_ERR_WORKSPACE: return "workspace too small";
+    case KVZ_ERR_HIP: return "HIP error";
+  }
+  return "unknown status";
+}
+
+size_t kvz_score_chunk_workspace(kvz_dtype dt, int H, int G, int n_in, int d, int n_c) {
+  if (H < 1 || G < 1 || n_in < 1 || n_c < 1 || (dt != KVZ_BF16 && dt != KVZ_F32)) return 0;
+  if ((long long)G * n_in > (1 << 20) || n_c > (1 << 24)) return 0;
+  return score_plan(dt, H, G, n_in, d, n_c).total_bytes;
+}
+
+kvz_status kvz_score_chunk(kvz_dtype dt, int H, int G, int d, int n_c, int n_prompt, int n_in,
+                           const void* q, const void* k_ctx, const void* k_in, float scale,
+                           float* S, void* ws, size_t ws_bytes, void* stream) {
+  if (dt != KVZ_BF16 && dt != KVZ_F32) return KVZ_ERR_UNSUPPORTED;
+  if (!head_dim_ok(d)) return KVZ_ERR_UNSUPPORTED;
+  if (H < 1 || G < 1 || n_in < 1 || n_c < 1 || n_prompt < 0 || n_prompt > n_in)
+    return KVZ_ERR_INVALID_ARG;
+  if ((long long)G * n_in > (1 << 20) || n_c > (1 << 24)) return KVZ_ERR_INVALID_ARG;
+  if (!q || !k_ctx || !k_in || !S || !ws) return KVZ_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(k_ctx) || !aligned16(k_in) || !aligned16(S))
+    return KVZ_ERR_INVALID_ARG;
+  if ((reinterpret_cast<uintptr_t>(ws) & 255u) != 0) return KVZ_ERR_INVALID_ARG;
+  if (!(scale > 0.f) || !isfinite(scale)) return KVZ_ERR_INVALID_ARG;
+  const ScorePlan p = score_plan(dt, H, G, n_in, d, n_c);
+  if (ws_bytes < p.total_bytes) return KVZ_ERR_WORKSPACE;
+  clear_error();
+  const hipError_t e = score_launch(dt, p, q, k_ctx, k_in, scale, S, ws,
+                                    reinterpret_cast<hipStream_t>(stream));
+  return e == hipSuccess ? KVZ_OK : KVZ_ERR_HIP;
+}
+
+int64_t kvz_keep_count(int64_t N, double r) {
+  if (N <= 0 || !(r > 0.0)) return 0;
+  if (r >= 1.0) return N;
+  const double k = floor(r * (double)N + 0.5);
+  if (k <= 0.0) return 0;
+  if (k >= (double)N) return N;
+  return (int64_t)k;
+}
+
+size_t kvz_select_workspace(int64_t n_heads, int n_c) {
+  if (n_heads < 1 || n_c < 1 || n_heads * (int64_t)n_c >= (int64_t(1) << 31)) return 0;
+  return select_plan(n_heads, n_c).total_bytes;
+}
+
+kvz_status kvz_select_threshold(const float* S, int64_t n_heads, int n_c, int64_t K,
+                                uint8_t* mask, int64_t* head_offsets, float* tau_out, void* ws,
+                                size_t ws_bytes, void* stream) {
+  if (n_heads < 1 || n_c < 1) return KVZ_ERR_INVALID_ARG;
+  const int64_t N = n_heads * (int64_t)n_c;
+  if (N >= (int64_t(1) << 31)) return KVZ_ERR_INVALID_ARG;
+  if (K < 0 || K > N) return KVZ_ERR_INVALID_ARG;
+  if (!S || !mask || !head_offsets || !tau_out || !ws) return KVZ_ERR_INVALID_ARG;
+  if (!aligned16(S) || (reinterpret_cast<uintptr_t>(head_offsets) & 7u) != 0 ||
+      (reinterpret_cast<uintptr_t>(tau_out) & 3u) != 0 ||
+      (reinterpret_cast<uintptr_t>(ws) & 255u) != 0)
+    return KVZ_ERR_INVALID_ARG;
+  const SelectPlan p = select_plan(n_heads, n_c);
+  if (ws_bytes < p.total_bytes) return KVZ_ERR_WORKSPACE;
+  clear_error();
+  const hipError_t e = select_launch(p, S, K, mask, head_offsets, tau_out, ws,
+                                     reinterpret_cast<hipStream_t>(stream));
+  return e == hipSuccess ? KVZ_OK : KVZ_ERR_HIP;
+}
+
+size_t kvz_compact_workspace(int64_t head_count, int n_c) {
+  if (head_count < 1 || n_c < 1) return 0;
+  return compact_plan(head_count, n_c).total_bytes;
+}
+
+kvz_status kvz_compact(kvz_dtype dt, int d, int n_c, int64_t head_begin, int64_t head_count,
+                       const void* k_ctx, const void* v_ctx, const uint8_t* mask,
+                       const int64_t* head_offsets, void* k_out, void* v_out, int32_t* idx_out,
+                       void* ws, size_t ws_bytes, void* stream) {
+  if (dt != KVZ_BF16 && dt != KVZ_F32) return KVZ_ERR_UNSUPPORTED;
+  if (!head_dim_ok(d)) return KVZ_ERR_UNSUPPORTED;
+  if (n_c < 1 || head_begin < 0 || head_count < 1) return KVZ_ERR_INVALID_ARG;
+  if ((head_begin + head_count) * (int64_t)n_c >= (int64_t(1) << 31)) return KVZ_ERR_INVALID_ARG;
+  if (!k_ctx || !v_ctx || !mask || !head_offsets || !k_out || !v_out || !idx_out || !ws)
+    return KVZ_ERR_INVALID_ARG;
+  if (!aligned16(k_ctx) || !aligned16(v_ctx) || !aligned16(k_out) || !aligned16(v_out) ||
+      (reinterpret_cast<uintptr_t>(head_offsets) & 7u) != 0 ||
+      (reinterpret_cast<uintptr_t>(idx_out) & 3u) != 0 ||
+      (reinterpret_cast<uintptr_t>(ws) & 255u) != 0)
+    return KVZ_ERR_INVALID_ARG;
+  const CompactPlan p = compact_plan(head_count, n_c);
+  if (ws_bytes < p.total_bytes) return KVZ_ERR_WORKSPACE;
+  const int row_bytes = d * (dt == KVZ_BF16 ? 2 : 4);
+  clear_error();
+  const hipError_t e = compact_launch(p, row_bytes, head_begin, k_ctx, v_ctx, mask, head_offsets,
+                                      k_out, v_out, idx_out, ws,
+                                      reinterpret_cast<hipStream_t>(stream));
+  return e == hipSuccess ? KVZ_OK : KVZ_ERR_HIP;
+}
+
+kvz_status kvz_prof_enable(int on, int max_launches) {
+  Prof& p = prof();
+  for (hipEvent_t e : p.pool) hipEventDestroy(e);
+  p.pool.clear();
+  p.recs.clear();
+  p.on = false;
+  p.pending = -1;
+  if (!on) return KVZ_OK;
+  if (max_launches < 1) return KVZ_ERR_INVALID_ARG;
+  p.pool.resize(2 * (size_t)max_launches);
+  for (auto& e : p.pool)
+    if (hipEventCreate(&e) != hipSuccess) return KVZ_ERR_HIP;
+  p.max_launches = max_launches;
+  p.recs.reserve(max_launches);
+  p.on = true;
+  return KVZ_OK;
+}
+
+kvz_status kvz_prof_read(const char* name, int64_t* launches, double* total_ms) {
+  if (!name || !launches || !total_ms) return KVZ_ERR_INVALID_ARG;
+  Prof& p = prof();
+  int64_t n = 0;
+  double ms = 0.0;
+  bool known = false;
+  static const char* kNames[] = {"score_pass1",   "score_combine",     "score_pass2",
+                                 "select_empty",  "select_init",       "select_hist",
+                                 "select_pick",   "select_tile_count", "select_scan",
+                                 "select_mask",   "compact_count",     "compact_scan",
+                                 "compact_scatter"};
+  for (const char* k : kNames) known |= strcmp(k, name) == 0;
+  if (!known) return KVZ_ERR_INVALID_ARG;
+  for (const ProfRec& r : p.recs) {
+    if (r.name != name) continue;
+    if (hipEventSynchronize(r.b) != hipSuccess) return KVZ_ERR_HIP;
+    float t = 0.f;
+    if (hipEventElapsedTime(&t, r.a, r.b) != hipSuccess) return KVZ_ERR_HIP;
+    ms += t;
+    ++n;
+  }
+  *launches = n;
+  *total_ms = ms;
+  return KVZ_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,91 @@
+// Shared device helpers and host-side launch plumbing for libkvz (gfx950).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/kvz.h"
+
+namespace kvz {
+
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(16))) float f32x16;
+
+constexpr int kNumXcd = 8;  // MI355X: 8 XCDs, workgroups dealt round-robin
+
+// Workgroup index remap so that consecutive logical indices share an XCD.
+// The hardware hands workgroup b to XCD (b % 8); the grid is padded to a
+// multiple of 8 and logical index = xcd * (grid / 8) + b / 8.  Logical
+// indices >= the real count must return immediately.
+__device__ __forceinline__ int xcd_logical_block() {
+  const int nb = gridDim.x;
+  const int per = nb / kNumXcd;
+  const int b = blockIdx.x;
+  return (b % kNumXcd) * per + b / kNumXcd;
+}
+
+inline int xcd_padded_grid(int n) { return (n + kNumXcd - 1) / kNumXcd * kNumXcd; }
+
+__device__ __forceinline__ uint4 ld16(const void* p) {
+  return *reinterpret_cast<const uint4*>(p);
+}
+
+__device__ __forceinline__ bf16x8 as_bf16x8(uint4 u) {
+  return __builtin_bit_cast(bf16x8, u);
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
+
+// ---------------------------------------------------------------------------
+// host side: launch timing hooks (see kvz_prof_enable in kvz.h)
+// ---------------------------------------------------------------------------
+void prof_before(const char* name, hipStream_t s);
+void prof_after(hipStream_t s);
+
+#define KVZ_LAUNCH(name, kern, grid, block, shmem, stream, ...)                     \
+  do {                                                                             \
+    ::kvz::prof_before(name, stream);                                              \
+    hipLaunchKernelGGL(kern, dim3(grid), dim3(block), shmem, stream, __VA_ARGS__); \
+    ::kvz::prof_after(stream);                                                     \
+  } while (0)
+
+// ---------------------------------------------------------------------------
+// internal launchers (argument validation happens in api.hip)
+// ---------------------------------------------------------------------------
+struct ScorePlan {
+  int H, G, d, n_c, n_in, R, R_pad;
+  int n_rt;             // pass-1 row tiles per head
+  int n_split_ctx;      // pass-1 splits of the context keys (+1 in-chunk split)
+  int tiles_per_split;  // 32-key tiles per context split
+  size_t part_bytes, lse_bytes, total_bytes;
+};
+ScorePlan score_plan(kvz_dtype dt, int H, int G, int n_in, int d, int n_c);
+hipError_t score_launch(kvz_dtype dt, const ScorePlan& p, const void* q, const void* kc,
+                        const void* kin, float scale, float* S, void* ws, hipStream_t st);
+
+struct SelectPlan {
+  int64_t N, n_heads;
+  int n_c, tiles_per_head;
+  int64_t n_tiles;
+  size_t total_bytes;
+};
+SelectPlan select_plan(int64_t n_heads, int n_c);
+hipError_t select_launch(const SelectPlan& p, const float* S, int64_t K, uint8_t* mask,
+                         int64_t* head_offsets, float* tau, void* ws, hipStream_t st);
+
+struct CompactPlan {
+  int64_t head_count;
+  int n_c, tiles_per_head;
+  int64_t n_tiles;
+  size_t total_bytes;
+};
+CompactPlan compact_plan(int64_t head_count, int n_c);
+hipError_t compact_launch(const CompactPlan& p, int row_bytes, int64_t head_begin,
+                          const void* kc, const void* vc, const uint8_t* mask,
+                          const int64_t* head_offsets, void* ko, void* vo, int32_t* idx,
+                          void* ws, hipStream_t st);
+
+inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+}  // namespace kvz

@@ -1,0 +1,513 @@
+// Reconstruction-attention scoring of one chunk (all KV heads of one layer).
+//
+// What is computed (KVzip blog post, sections 4.3.1 and 4.3.2; paperhub
+// rebuttal, answer on positional OOD): for every KV head h, query head g of
+// its group and query row i of the chunk, p = softmax(scale * q . k) over all
+// n_c context keys followed by the chunk's own keys 0..i; the score of
+// context key j is the running max over chunks of max_{g,i} p[j].
+//
+// Two passes, neither of which materialises the (G*n_in) x (n_c + n_in)
+// probability matrix (the blog's section 4.4 explains why a FlashAttention
+// kernel that only returns P*V cannot give max_i softmax):
+//   pass 1  per query row, lse = log2 sum_j 2^(x_j * scale * log2 e) over the
+//           visible keys, by an online max/sum over 32-key tiles; the key
+//           axis is split over workgroups and merged by score_combine;
+//   pass 2  per context key, t_j = max over rows (x * scale * log2 e - lse),
+//           then S_j = max(S_j, 2^t_j).  max_i 2^(y_i) = 2^(max_i y_i), so
+//           pass 2 needs one exp per key, not per logit.
+// Query rows are packed i-major (r = i*G + g) so that a tile of consecutive
+// rows shares nearly the same causal limit.
+//
+// bf16 path: 32x32x16 bf16 MFMA with fp32 accumulation, K (pass 1) or Q
+// (pass 2) tiles staged in LDS with an XOR swizzle of 16-byte chunks, the
+// other operand held in registers for the whole key or row sweep.  Pass 1
+// computes K*Q^T (keys on the MFMA row axis) so its reduction over keys is
+// in-lane; pass 2 computes Q*K^T so its reduction over rows is in-lane.
+// fp32 path: plain VALU kernels for small fp32 problems.
+#include <math.h>
+
+#include "common.h"
+
+namespace kvz {
+
+namespace {
+
+constexpr int KT = 32;          // keys per pass-1 tile
+constexpr int P1_ROWS = 256;    // query rows per pass-1 workgroup (4 waves x 64)
+constexpr int P2_KEYS = 256;    // context keys per pass-2 workgroup (4 waves x 64)
+constexpr int P2_RS = 64;       // query rows per pass-2 LDS stage
+constexpr float kNegBig = -1e30f;
+
+template <int D>
+struct Geo {
+  static constexpr int KS = D / 16;                 // MFMA k-steps over d
+  static constexpr int CH = D / 8;                  // 16-byte chunks per row
+  static constexpr int SWZ = (CH < 16 ? CH : 16) - 1;
+};
+
+template <int CH, int SWZ>
+__device__ __forceinline__ int swz(int row, int ch) {
+  return row * CH + (ch ^ (row & SWZ));
+}
+
+// Online max/sum of 16 logits (raw dot products) into (m, l), log2 domain.
+__device__ __forceinline__ void online_update(const f32x16& a, float& m, float& l, float cl2) {
+  float mx = a[0];
+#pragma unroll
+  for (int v = 1; v < 16; ++v) mx = fmaxf(mx, a[v]);
+  const float mn = fmaxf(m, mx * cl2);
+  float s0 = 0.f, s1 = 0.f, s2 = 0.f, s3 = 0.f;
+#pragma unroll
+  for (int v = 0; v < 16; v += 4) {
+    s0 += fast_exp2(fmaf(a[v + 0], cl2, -mn));
+    s1 += fast_exp2(fmaf(a[v + 1], cl2, -mn));
+    s2 += fast_exp2(fmaf(a[v + 2], cl2, -mn));
+    s3 += fast_exp2(fmaf(a[v + 3], cl2, -mn));
+  }
+  l = l * fast_exp2(m - mn) + ((s0 + s1) + (s2 + s3));
+  m = mn;
+}
+
+// Row index (within a 32x32 MFMA output tile) held by accumulator v of a lane.
+__device__ __forceinline__ int acc_row(int v, int half) {
+  return 8 * (v >> 2) + 4 * half + (v & 3);
+}
+
+// ---------------------------------------------------------------------------
+// pass 1, bf16: partial (max, sum) per query row and key split
+// grid: H x splits x row-tiles (XCD-remapped: head-major, row tile fastest)
+// ---------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(256) void score_pass1_bf16(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ kc,
+    const uint16_t* __restrict__ kin, float2* __restrict__ part, int G, int n_c, int n_in,
+    int R, int R_pad, int n_rt, int n_split_ctx, int tiles_per_split, float cl2,
+    int n_blocks) {
+  constexpr int KS = Geo<D>::KS, CH = Geo<D>::CH, SWZ = Geo<D>::SWZ;
+  constexpr int LOADS = KT * CH / 256;
+  __shared__ uint4 lds[2][KT * CH];
+
+  const int lb = xcd_logical_block();
+  if (lb >= n_blocks) return;
+  const int splits = n_split_ctx + 1;
+  const int rt = lb % n_rt;
+  const int s = (lb / n_rt) % splits;
+  const int h = lb / (n_rt * splits);
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int n = lane & 31, half = lane >> 5;
+
+  const bool inchunk = (s == n_split_ctx);
+  const uint16_t* kbase;
+  int nkeys, t_begin, t_end;
+  if (!inchunk) {
+    kbase = kc + (size_t)h * n_c * D;
+    nkeys = n_c;
+    const int n_tiles_ctx = (n_c + KT - 1) / KT;
+    t_begin = s * tiles_per_split;
+    t_end = min(n_tiles_ctx, t_begin + tiles_per_split);
+  } else {
+    kbase = kin + (size_t)h * n_in * D;
+    nkeys = n_in;
+    const int rlast = min(R, (rt + 1) * P1_ROWS) - 1;
+    t_begin = 0;
+    t_end = (rlast / G) / KT + 1;
+  }
+
+  // stationary query operand (B of K*Q^T): this lane's query column n
+  bf16x8 qr[2][KS];
+  int irow[2];
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    const int r = rt * P1_ROWS + wave * 64 + t * 32 + n;
+    irow[t] = r / G;
+    if (r < R) {
+      const int g = r - irow[t] * G;
+      const uint16_t* p = q + ((size_t)(h * G + g) * n_in + irow[t]) * D + half * 8;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) qr[t][ks] = as_bf16x8(ld16(p + ks * 16));
+    } else {
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) qr[t][ks] = as_bf16x8(make_uint4(0, 0, 0, 0));
+    }
+  }
+
+  float m[2] = {kNegBig, kNegBig}, l[2] = {0.f, 0.f};
+
+  if (t_begin < t_end) {
+    uint4 reg[LOADS];
+    auto load_tile = [&](int tile) {
+#pragma unroll
+      for (int u = 0; u < LOADS; ++u) {
+        const int c = tid + 256 * u, row = c / CH, ch = c % CH, key = tile * KT + row;
+        reg[u] = key < nkeys ? ld16(kbase + (size_t)key * D + ch * 8) : make_uint4(0, 0, 0, 0);
+      }
+    };
+    auto store_tile = [&](int buf) {
+#pragma unroll
+      for (int u = 0; u < LOADS; ++u) {
+        const int c = tid + 256 * u, row = c / CH, ch = c % CH;
+        lds[buf][swz<CH, SWZ>(row, ch)] = reg[u];
+      }
+    };
+    load_tile(t_begin);
+    store_tile(0);
+    __syncthreads();
+    for (int it = t_begin; it < t_end; ++it) {
+      const int buf = (it - t_begin) & 1;
+      const bool more = it + 1 < t_end;
+      if (more) load_tile(it + 1);
+      f32x16 acc0 = {}, acc1 = {};
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const bf16x8 a = as_bf16x8(lds[buf][swz<CH, SWZ>(n, ks * 2 + half)]);
+        acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qr[0][ks], acc0, 0, 0, 0);
+        acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qr[1][ks], acc1, 0, 0, 0);
+      }
+      const int key0 = it * KT;
+      if (inchunk) {
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int key = key0 + acc_row(v, half);
+          if (key > irow[0]) acc0[v] = -INFINITY;
+          if (key > irow[1]) acc1[v] = -INFINITY;
+        }
+      } else if (key0 + KT > n_c) {
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          if (key0 + acc_row(v, half) >= n_c) {
+            acc0[v] = -INFINITY;
+            acc1[v] = -INFINITY;
+          }
+        }
+      }
+      online_update(acc0, m[0], l[0], cl2);
+      online_update(acc1, m[1], l[1], cl2);
+      if (more) store_tile(buf ^ 1);
+      __syncthreads();
+    }
+  }
+
+  // lanes n and n+32 hold the same query column, different key rows
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    const float mo = __shfl_xor(m[t], 32);
+    const float lo = __shfl_xor(l[t], 32);
+    const float M = fmaxf(m[t], mo);
+    const float L = l[t] * fast_exp2(m[t] - M) + lo * fast_exp2(mo - M);
+    if (half == 0) {
+      const int r = rt * P1_ROWS + wave * 64 + t * 32 + n;
+      part[((size_t)h * splits + s) * R_pad + r] = make_float2(M, L);
+    }
+  }
+}
+
+// merge the key splits: lse2 = M + log2(sum_s l_s 2^(m_s - M)); padding rows
+// get +inf so that pass 2 ignores them.
+__global__ __launch_bounds__(256) void score_combine(const float2* __restrict__ part,
+                                                     float* __restrict__ lse2, int splits,
+                                                     int R, int R_pad, int H) {
+  const int idx = blockIdx.x * 256 + threadIdx.x;
+  if (idx >= H * R_pad) return;
+  const int h = idx / R_pad, r = idx - h * R_pad;
+  if (r >= R) {
+    lse2[idx] = INFINITY;
+    return;
+  }
+  const float2* p = part + (size_t)h * splits * R_pad + r;
+  float M = kNegBig;
+  for (int s = 0; s < splits; ++s) M = fmaxf(M, p[(size_t)s * R_pad].x);
+  float L = 0.f;
+  for (int s = 0; s < splits; ++s) {
+    const float2 v = p[(size_t)s * R_pad];
+    L += v.y * exp2f(v.x - M);
+  }
+  lse2[idx] = M + log2f(L);
+}
+
+// ---------------------------------------------------------------------------
+// pass 2, bf16: column max over all query rows, running max into S
+// grid: H x key-tiles of 256 (XCD-remapped: head-major)
+// ---------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(256) void score_pass2_bf16(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ kc,
+    const float* __restrict__ lse2, float* __restrict__ S, int G, int n_c, int n_in, int R,
+    int R_pad, int n_kt, float cl2, int n_blocks) {
+  constexpr int KS = Geo<D>::KS, CH = Geo<D>::CH, SWZ = Geo<D>::SWZ;
+  constexpr int LOADS = P2_RS * CH / 256;
+  __shared__ uint4 ldq[2][P2_RS * CH];
+  __shared__ float4 ldl[2][P2_RS / 4];
+
+  const int lb = xcd_logical_block();
+  if (lb >= n_blocks) return;
+  const int kt = lb % n_kt;
+  const int h = lb / n_kt;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int n = lane & 31, half = lane >> 5;
+  const int j0 = kt * P2_KEYS + wave * 64;
+
+  // stationary key operand (B of Q*K^T): this lane's key column n
+  bf16x8 kr[2][KS];
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    const int j = j0 + t * 32 + n;
+    if (j < n_c) {
+      const uint16_t* p = kc + ((size_t)h * n_c + j) * D + half * 8;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) kr[t][ks] = as_bf16x8(ld16(p + ks * 16));
+    } else {
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) kr[t][ks] = as_bf16x8(make_uint4(0, 0, 0, 0));
+    }
+  }
+
+  const float* lseh = lse2 + (size_t)h * R_pad;
+  const int n_stages = R_pad / P2_RS;
+  uint4 reg[LOADS];
+  float4 lreg = make_float4(0.f, 0.f, 0.f, 0.f);
+  auto load_stage = [&](int st) {
+    const int r0 = st * P2_RS;
+#pragma unroll
+    for (int u = 0; u < LOADS; ++u) {
+      const int c = tid + 256 * u, row = c / CH, ch = c % CH, r = r0 + row;
+      if (r < R) {
+        const int i = r / G, g = r - i * G;
+        reg[u] = ld16(q + ((size_t)(h * G + g) * n_in + i) * D + ch * 8);
+      } else {
+        reg[u] = make_uint4(0, 0, 0, 0);
+      }
+    }
+    if (tid < P2_RS / 4) lreg = reinterpret_cast<const float4*>(lseh + r0)[tid];
+  };
+  auto store_stage = [&](int buf) {
+#pragma unroll
+    for (int u = 0; u < LOADS; ++u) {
+      const int c = tid + 256 * u, row = c / CH, ch = c % CH;
+      ldq[buf][swz<CH, SWZ>(row, ch)] = reg[u];
+    }
+    if (tid < P2_RS / 4) ldl[buf][tid] = lreg;
+  };
+
+  float mx0 = -INFINITY, mx1 = -INFINITY;
+  load_stage(0);
+  store_stage(0);
+  __syncthreads();
+  for (int st = 0; st < n_stages; ++st) {
+    const int buf = st & 1;
+    const bool more = st + 1 < n_stages;
+    if (more) load_stage(st + 1);
+#pragma unroll
+    for (int sub = 0; sub < 2; ++sub) {
+      f32x16 acc0 = {}, acc1 = {};
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const bf16x8 a = as_bf16x8(ldq[buf][swz<CH, SWZ>(sub * 32 + n, ks * 2 + half)]);
+        acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, kr[0][ks], acc0, 0, 0, 0);
+        acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, kr[1][ks], acc1, 0, 0, 0);
+      }
+#pragma unroll
+      for (int vg = 0; vg < 4; ++vg) {
+        const float4 L4 = ldl[buf][(sub * 32 + 8 * vg + 4 * half) >> 2];
+        const float lv[4] = {L4.x, L4.y, L4.z, L4.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int v = vg * 4 + e;
+          mx0 = fmaxf(mx0, fmaf(acc0[v], cl2, -lv[e]));
+          mx1 = fmaxf(mx1, fmaf(acc1[v], cl2, -lv[e]));
+        }
+      }
+    }
+    if (more) store_stage(buf ^ 1);
+    __syncthreads();
+  }
+
+  mx0 = fmaxf(mx0, __shfl_xor(mx0, 32));
+  mx1 = fmaxf(mx1, __shfl_xor(mx1, 32));
+  if (half == 0) {
+    const float mxs[2] = {mx0, mx1};
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const int j = j0 + t * 32 + n;
+      if (j < n_c) {
+        float* sp = S + (size_t)h * n_c + j;
+        *sp = fmaxf(*sp, fminf(fast_exp2(mxs[t]), 1.0f));
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// fp32 path (VALU): one thread per query row (pass 1) / per context key (pass 2)
+// ---------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(64) void score_pass1_f32(const float* __restrict__ q,
+                                                      const float* __restrict__ kc,
+                                                      const float* __restrict__ kin,
+                                                      float* __restrict__ lse2, int G, int n_c,
+                                                      int n_in, int R, int R_pad, float cl2) {
+  __shared__ float ldq[D][64];
+  __shared__ float ldk[KT][D + 1];
+  const int h = blockIdx.y;
+  const int tid = threadIdx.x;
+  const int r = blockIdx.x * 64 + tid;
+  const int i = r / G, g = r - (r / G) * G;
+  for (int k = 0; k < D; ++k)
+    ldq[k][tid] = (r < R) ? q[((size_t)(h * G + g) * n_in + i) * D + k] : 0.f;
+  float m = kNegBig, l = 0.f;
+  const int n_ctx_tiles = (n_c + KT - 1) / KT;
+  const int imax = (min(R, (int)(blockIdx.x + 1) * 64) - 1) / G;
+  const int n_tiles = n_ctx_tiles + imax / KT + 1;
+  for (int tile = 0; tile < n_tiles; ++tile) {
+    const bool ctx = tile < n_ctx_tiles;
+    const int key0 = ctx ? tile * KT : (tile - n_ctx_tiles) * KT;
+    const float* kb = ctx ? kc + (size_t)h * n_c * D : kin + (size_t)h * n_in * D;
+    const int nk = ctx ? n_c : n_in;
+    __syncthreads();
+    for (int e = tid; e < KT * D; e += 64) {
+      const int kk = e / D, dd = e - kk * D;
+      ldk[kk][dd] = (key0 + kk < nk) ? kb[(size_t)(key0 + kk) * D + dd] : 0.f;
+    }
+    __syncthreads();
+    for (int kk = 0; kk < KT; ++kk) {
+      const int key = key0 + kk;
+      const bool vis = ctx ? key < n_c : key <= i;
+      if (!vis) continue;
+      float dot = 0.f;
+      for (int k = 0; k < D; ++k) dot = fmaf(ldq[k][tid], ldk[kk][k], dot);
+      const float x = dot * cl2;
+      const float mn = fmaxf(m, x);
+      l = l * exp2f(m - mn) + exp2f(x - mn);
+      m = mn;
+    }
+  }
+  if (r < R_pad) lse2[(size_t)h * R_pad + r] = (r < R) ? m + log2f(l) : INFINITY;
+}
+
+template <int D>
+__global__ __launch_bounds__(64) void score_pass2_f32(const float* __restrict__ q,
+                                                      const float* __restrict__ kc,
+                                                      const float* __restrict__ lse2,
+                                                      float* __restrict__ S, int G, int n_c,
+                                                      int n_in, int R, int R_pad, float cl2) {
+  __shared__ float ldk[D][64];
+  __shared__ float ldq[32][D + 1];
+  __shared__ float ldl[32];
+  const int h = blockIdx.y;
+  const int tid = threadIdx.x;
+  const int j = blockIdx.x * 64 + tid;
+  for (int k = 0; k < D; ++k)
+    ldk[k][tid] = (j < n_c) ? kc[((size_t)h * n_c + j) * D + k] : 0.f;
+  float mx = -INFINITY;
+  for (int r0 = 0; r0 < R; r0 += 32) {
+    __syncthreads();
+    for (int e = tid; e < 32 * D; e += 64) {
+      const int rr = e / D, dd = e - rr * D, r = r0 + rr;
+      float v = 0.f;
+      if (r < R) {
+        const int i = r / G, g = r - i * G;
+        v = q[((size_t)(h * G + g) * n_in + i) * D + dd];
+      }
+      ldq[rr][dd] = v;
+    }
+    if (tid < 32) ldl[tid] = lse2[(size_t)h * R_pad + r0 + tid];
+    __syncthreads();
+    for (int rr = 0; rr < 32 && r0 + rr < R; ++rr) {
+      float dot = 0.f;
+      for (int k = 0; k < D; ++k) dot = fmaf(ldq[rr][k], ldk[k][tid], dot);
+      mx = fmaxf(mx, dot * cl2 - ldl[rr]);
+    }
+  }
+  if (j < n_c) {
+    float* sp = S + (size_t)h * n_c + j;
+    *sp = fmaxf(*sp, fminf(exp2f(mx), 1.0f));
+  }
+}
+
+template <int D>
+hipError_t launch_bf16(const ScorePlan& p, const void* q, const void* kc, const void* kin,
+                       float cl2, float* S, void* ws, hipStream_t st) {
+  float2* part = reinterpret_cast<float2*>(ws);
+  float* lse2 = reinterpret_cast<float*>(reinterpret_cast<char*>(ws) + p.part_bytes);
+  const int splits = p.n_split_ctx + 1;
+  const int nb1 = p.H * splits * p.n_rt;
+  KVZ_LAUNCH("score_pass1", score_pass1_bf16<D>, xcd_padded_grid(nb1), 256, 0, st,
+             (const uint16_t*)q, (const uint16_t*)kc, (const uint16_t*)kin, part, p.G, p.n_c,
+             p.n_in, p.R, p.R_pad, p.n_rt, p.n_split_ctx, p.tiles_per_split, cl2, nb1);
+  const int nc = p.H * p.R_pad;
+  KVZ_LAUNCH("score_combine", score_combine, (nc + 255) / 256, 256, 0, st, part, lse2, splits,
+             p.R, p.R_pad, p.H);
+  const int n_kt = (p.n_c + P2_KEYS - 1) / P2_KEYS;
+  const int nb2 = p.H * n_kt;
+  KVZ_LAUNCH("score_pass2", score_pass2_bf16<D>, xcd_padded_grid(nb2), 256, 0, st,
+             (const uint16_t*)q, (const uint16_t*)kc, lse2, S, p.G, p.n_c, p.n_in, p.R,
+             p.R_pad, n_kt, cl2, nb2);
+  return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_f32(const ScorePlan& p, const void* q, const void* kc, const void* kin,
+                      float cl2, float* S, void* ws, hipStream_t st) {
+  float* lse2 = reinterpret_cast<float*>(ws);
+  dim3 g1((p.R + 63) / 64, p.H);
+  KVZ_LAUNCH("score_pass1", score_pass1_f32<D>, g1, 64, 0, st, (const float*)q,
+             (const float*)kc, (const float*)kin, lse2, p.G, p.n_c, p.n_in, p.R, p.R_pad, cl2);
+  dim3 g2((p.n_c + 63) / 64, p.H);
+  KVZ_LAUNCH("score_pass2", score_pass2_f32<D>, g2, 64, 0, st, (const float*)q,
+             (const float*)kc, lse2, S, p.G, p.n_c, p.n_in, p.R, p.R_pad, cl2);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+ScorePlan score_plan(kvz_dtype dt, int H, int G, int n_in, int d, int n_c) {
+  ScorePlan p{};
+  p.H = H;
+  p.G = G;
+  p.d = d;
+  p.n_c = n_c;
+  p.n_in = n_in;
+  p.R = G * n_in;
+  p.n_rt = (p.R + P1_ROWS - 1) / P1_ROWS;
+  p.R_pad = p.n_rt * P1_ROWS;
+  const int n_ctx_tiles = (n_c + KT - 1) / KT;
+  if (dt == KVZ_BF16) {
+    // enough workgroups to cover the chip a few times, at least 16 tiles each
+    int want = (2048 + H * p.n_rt - 1) / (H * p.n_rt);
+    int maxs = n_ctx_tiles / 16;
+    if (maxs < 1) maxs = 1;
+    if (want > maxs) want = maxs;
+    if (want < 1) want = 1;
+    p.tiles_per_split = (n_ctx_tiles + want - 1) / want;
+    p.n_split_ctx = (n_ctx_tiles + p.tiles_per_split - 1) / p.tiles_per_split;
+    p.part_bytes = align256((size_t)H * (p.n_split_ctx + 1) * p.R_pad * sizeof(float2));
+  } else {
+    p.tiles_per_split = n_ctx_tiles;
+    p.n_split_ctx = 1;
+    p.part_bytes = 0;
+  }
+  p.lse_bytes = align256((size_t)H * p.R_pad * sizeof(float));
+  p.total_bytes = p.part_bytes + p.lse_bytes;
+  return p;
+}
+
+hipError_t score_launch(kvz_dtype dt, const ScorePlan& p, const void* q, const void* kc,
+                        const void* kin, float scale, float* S, void* ws, hipStream_t st) {
+  const float cl2 = scale * 1.4426950408889634f;
+  if (dt == KVZ_BF16) {
+    switch (p.d) {
+      case 64: return launch_bf16<64>(p, q, kc, kin, cl2, S, ws, st);
+      case 128: return launch_bf16<128>(p, q, kc, kin, cl2, S, ws, st);
+      case 256: return launch_bf16<256>(p, q, kc, kin, cl2, S, ws, st);
+    }
+  } else {
+    switch (p.d) {
+      case 64: return launch_f32<64>(p, q, kc, kin, cl2, S, ws, st);
+      case 128: return launch_f32<128>(p, q, kc, kin, cl2, S, ws, st);
+      case 256: return launch_f32<256>(p, q, kc, kin, cl2, S, ws, st);
+    }
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace kvz

@@ -1,0 +1,203 @@
+"""Python binding of libkvz (ctypes): argument marshalling only.
+
+Every function here has the name of the C entry point it calls (include/kvz.h)
+and forwards torch tensors as raw device pointers together with the current
+HIP stream.  No arithmetic of the method happens in Python.  If libkvz.so has
+not been built, loading fails loudly; there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libkvz.so")
+
+KVZ_OK, KVZ_ERR_INVALID_ARG, KVZ_ERR_UNSUPPORTED, KVZ_ERR_WORKSPACE, KVZ_ERR_HIP = range(5)
+KVZ_BF16, KVZ_F32 = 0, 1
+
+# every symbol declared in include/kvz.h
+SYMBOLS = (
+    "kvz_status_string", "kvz_score_chunk_workspace", "kvz_score_chunk", "kvz_keep_count",
+    "kvz_select_workspace", "kvz_select_threshold", "kvz_compact_workspace", "kvz_compact",
+    "kvz_prof_enable", "kvz_prof_read",
+)
+
+_lib = None
+
+
+class KvzError(RuntimeError):
+    def __init__(self, status, where):
+        self.status = status
+        super().__init__(f"{where}: {kvz_status_string(status)} (status {status})")
+
+
+def lib():
+    """Load libkvz.so (once) and declare its signatures."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(
+            f"{LIB_PATH} is missing: build it with `python -c 'import __graft_entry__ as g; g.build()'`"
+            " (the HIP library is required; there is no CPU fallback)")
+    L = ctypes.CDLL(LIB_PATH)
+    c_int, c_i64, c_sz, c_f, c_d, c_p = (ctypes.c_int, ctypes.c_int64, ctypes.c_size_t,
+                                         ctypes.c_float, ctypes.c_double, ctypes.c_void_p)
+    L.kvz_status_string.argtypes = [c_int]
+    L.kvz_status_string.restype = ctypes.c_char_p
+    L.kvz_score_chunk_workspace.argtypes = [c_int, c_int, c_int, c_int, c_int, c_int]
+    L.kvz_score_chunk_workspace.restype = c_sz
+    L.kvz_score_chunk.argtypes = [c_int, c_int, c_int, c_int, c_int, c_int, c_int, c_p, c_p, c_p,
+                                  c_f, c_p, c_p, c_sz, c_p]
+    L.kvz_score_chunk.restype = c_int
+    L.kvz_keep_count.argtypes = [c_i64, c_d]
+    L.kvz_keep_count.restype = c_i64
+    L.kvz_select_workspace.argtypes = [c_i64, c_int]
+    L.kvz_select_workspace.restype = c_sz
+    L.kvz_select_threshold.argtypes = [c_p, c_i64, c_int, c_i64, c_p, c_p, c_p, c_p, c_sz, c_p]
+    L.kvz_select_threshold.restype = c_int
+    L.kvz_compact_workspace.argtypes = [c_i64, c_int]
+    L.kvz_compact_workspace.restype = c_sz
+    L.kvz_compact.argtypes = [c_int, c_int, c_int, c_i64, c_i64, c_p, c_p, c_p, c_p, c_p, c_p, c_p,
+                              c_p, c_sz, c_p]
+    L.kvz_compact.restype = c_int
+    L.kvz_prof_enable.argtypes = [c_int, c_int]
+    L.kvz_prof_enable.restype = c_int
+    L.kvz_prof_read.argtypes = [ctypes.c_char_p, ctypes.POINTER(c_i64), ctypes.POINTER(c_d)]
+    L.kvz_prof_read.restype = c_int
+    _lib = L
+    return L
+
+
+def _check(status, where):
+    if status != KVZ_OK:
+        raise KvzError(status, where)
+
+
+def _stream(stream):
+    import torch
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _dtype_code(t):
+    import torch
+    if t.dtype == torch.bfloat16:
+        return KVZ_BF16
+    if t.dtype == torch.float32:
+        return KVZ_F32
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _ptr(t, name):
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _ws(nbytes, device):
+    import torch
+    # uint8 storage; the caching allocator returns >= 256-byte aligned blocks
+    return torch.empty(max(int(nbytes), 256), dtype=torch.uint8, device=device)
+
+
+def kvz_status_string(status: int) -> str:
+    return lib().kvz_status_string(int(status)).decode()
+
+
+def kvz_keep_count(n_total: int, ratio: float) -> int:
+    return int(lib().kvz_keep_count(int(n_total), float(ratio)))
+
+
+def kvz_score_chunk_workspace(dtype_code, H, G, n_in, d, n_c) -> int:
+    return int(lib().kvz_score_chunk_workspace(dtype_code, H, G, n_in, d, n_c))
+
+
+def kvz_select_workspace(n_heads, n_c) -> int:
+    return int(lib().kvz_select_workspace(int(n_heads), int(n_c)))
+
+
+def kvz_compact_workspace(head_count, n_c) -> int:
+    return int(lib().kvz_compact_workspace(int(head_count), int(n_c)))
+
+
+def kvz_score_chunk(q, k_ctx, k_in, S, n_prompt, scale=None, ws=None, stream=None):
+    """One reconstruction chunk of one layer.  q [H][G][n_in][d], k_ctx
+    [H][n_c][d], k_in [H][n_in][d] (bf16 or fp32), S [H][n_c] fp32 in/out."""
+    import torch
+    H, G, n_in, d = q.shape
+    n_c = k_ctx.shape[1]
+    if tuple(k_ctx.shape) != (H, n_c, d) or tuple(k_in.shape) != (H, n_in, d):
+        raise ValueError("shape mismatch between q, k_ctx and k_in")
+    if tuple(S.shape) != (H, n_c) or S.dtype != torch.float32:
+        raise ValueError("S must be fp32 [H][n_c]")
+    if k_ctx.dtype != q.dtype or k_in.dtype != q.dtype:
+        raise TypeError("q, k_ctx and k_in must share a dtype")
+    dt = _dtype_code(q)
+    if scale is None:
+        scale = d ** -0.5
+    need = kvz_score_chunk_workspace(dt, H, G, n_in, d, n_c)
+    if ws is None:
+        ws = _ws(need, q.device)
+    st = lib().kvz_score_chunk(dt, H, G, d, n_c, int(n_prompt), n_in, _ptr(q, "q"),
+                               _ptr(k_ctx, "k_ctx"), _ptr(k_in, "k_in"), float(scale),
+                               _ptr(S, "S"), _ptr(ws, "ws"), ws.numel() * ws.element_size(),
+                               _stream(stream))
+    _check(st, "kvz_score_chunk")
+    return S
+
+
+def kvz_select_threshold(S, K, mask=None, head_offsets=None, tau=None, ws=None, stream=None):
+    """Exact top-K over S [n_heads][n_c] (fp32).  Returns (mask uint8 [N],
+    head_offsets int64 [n_heads + 1], tau fp32 [1]), all on the device."""
+    import torch
+    n_heads, n_c = S.shape
+    dev = S.device
+    if mask is None:
+        mask = torch.empty(n_heads * n_c, dtype=torch.uint8, device=dev)
+    if head_offsets is None:
+        head_offsets = torch.empty(n_heads + 1, dtype=torch.int64, device=dev)
+    if tau is None:
+        tau = torch.empty(1, dtype=torch.float32, device=dev)
+    if ws is None:
+        ws = _ws(kvz_select_workspace(n_heads, n_c), dev)
+    st = lib().kvz_select_threshold(_ptr(S, "S"), n_heads, n_c, int(K), _ptr(mask, "mask"),
+                                    _ptr(head_offsets, "head_offsets"), _ptr(tau, "tau"),
+                                    _ptr(ws, "ws"), ws.numel() * ws.element_size(),
+                                    _stream(stream))
+    _check(st, "kvz_select_threshold")
+    return mask, head_offsets, tau
+
+
+def kvz_compact(k_ctx, v_ctx, mask, head_offsets, k_out, v_out, idx_out, head_begin=0,
+                ws=None, stream=None):
+    """Pack heads [head_begin, head_begin + k_ctx.shape[0]) of the kept rows.
+    k_ctx, v_ctx [head_count][n_c][d]; k_out, v_out [K][d]; idx_out int32 [K]."""
+    head_count, n_c, d = k_ctx.shape
+    dt = _dtype_code(k_ctx)
+    if v_ctx.shape != k_ctx.shape or v_ctx.dtype != k_ctx.dtype:
+        raise ValueError("k_ctx and v_ctx must match")
+    if ws is None:
+        ws = _ws(kvz_compact_workspace(head_count, n_c), k_ctx.device)
+    st = lib().kvz_compact(dt, d, n_c, int(head_begin), head_count, _ptr(k_ctx, "k_ctx"),
+                           _ptr(v_ctx, "v_ctx"), _ptr(mask, "mask"),
+                           _ptr(head_offsets, "head_offsets"), _ptr(k_out, "k_out"),
+                           _ptr(v_out, "v_out"), _ptr(idx_out, "idx_out"), _ptr(ws, "ws"),
+                           ws.numel() * ws.element_size(), _stream(stream))
+    _check(st, "kvz_compact")
+    return k_out, v_out, idx_out
+
+
+def kvz_prof_enable(on: bool, max_launches: int = 1 << 16):
+    _check(lib().kvz_prof_enable(1 if on else 0, int(max_launches)), "kvz_prof_enable")
+
+
+def kvz_prof_read(name: str):
+    """(launches, total_ms) of one kernel name since kvz_prof_enable."""
+    n = ctypes.c_int64()
+    ms = ctypes.c_double()
+    _check(lib().kvz_prof_read(name.encode(), ctypes.byref(n), ctypes.byref(ms)), "kvz_prof_read")
+    return int(n.value), float(ms.value)

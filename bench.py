@@ -1,0 +1,239 @@
+"""Throughput of the whole hot path on one MI355X.
+
+One step = score every reconstruction chunk of every layer of the cache
+(kvz_score_chunk, L x n_chunks calls), select the global keep set
+(kvz_select_threshold) and compact the kept K/V rows (kvz_compact), on
+synthetic inputs already resident in device memory.
+
+Prints one JSON line: context tokens scored and compacted per second, the
+roofline of the dominant kernel (from HIP events recorded around each launch
+inside the timed steps) and the CPU oracle's rate on a bounded sample.
+"""
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+MFMA_BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16
+HBM_PEAK_GBS = 8000.0
+METRIC = "context tokens scored+compacted/sec (8B shape, 128K ctx); % bf16 MFMA peak"
+
+
+def score_flops(wl, n_in):
+    """Algorithmic flops of one kvz_score_chunk call: one q.k product (2d
+    flops) per visible (row, key) pair, pass 1 over context + causal chunk
+    keys, pass 2 over context keys."""
+    H, G, d, n_c = wl.heads, wl.group, wl.head_dim, wl.n_ctx
+    vis_rows = G * (n_in * n_c + n_in * (n_in + 1) // 2)
+    p1 = 2 * d * H * vis_rows
+    p2 = 2 * d * H * G * n_in * n_c
+    return p1, p2
+
+
+def cpu_baseline(wl, budget_s):
+    """The oracle as it stands on a bounded sample: one (layer, head) pair,
+    as many whole chunks as fit in about budget_s seconds; the full step is
+    extrapolated linearly in (layer, head, chunk) units."""
+    import numpy as np
+    from attention_score_reduction_amd.inputs import HostGen
+    from oracle import ras
+
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:  # pragma: no cover
+        threads = os.cpu_count() or 1
+    gen = HostGen(wl)
+    kc, _ = gen.context(0, [0])
+    kc64 = ras.to_f64(kc, wl.dtype)
+    S = np.zeros((1, wl.n_ctx))
+    scale = 1 / math.sqrt(wl.head_dim)
+    done = 0
+    t_total = 0.0
+    n_chunks = len(wl.chunks())
+    while done < n_chunks:
+        q, kin = gen.chunk_inputs(0, done, [0])
+        q64, k64 = ras.to_f64(q, wl.dtype), ras.to_f64(kin, wl.dtype)
+        t0 = time.perf_counter()
+        ras.score_chunk(q64, kc64, k64, scale, S)
+        t_total += time.perf_counter() - t0
+        done += 1
+        if t_total > budget_s:
+            break
+    units_full = wl.layers * wl.heads * n_chunks
+    t_full = t_total / done * units_full
+    return {"value": wl.n_ctx / t_full, "unit": "context tokens/s", "cores": threads,
+            "kind": "oracle",
+            "sample": f"scoring of {done} of {n_chunks} chunks for 1 of {wl.layers * wl.heads} "
+                      f"(layer, head) pairs in {t_total:.1f} s, extrapolated x{units_full / done:.0f} "
+                      f"to the full step (selection and compaction not included)"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=2)
+    ap.add_argument("--warmup", type=int, default=1)
+    ap.add_argument("--workload", default="llama8b_128k")
+    ap.add_argument("--layers", type=int, default=None, help="fewer layers (debug only)")
+    ap.add_argument("--cpu-seconds", type=float, default=20.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
+              "(the per-head scoring would shard across GPUs without communication, but no "
+              "multi-GPU path is built)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import attention_score_reduction_amd as kvz
+    from attention_score_reduction_amd.inputs import WORKLOADS, device_tensors
+
+    wl = WORKLOADS[args.workload]
+    if args.layers:
+        wl = wl.with_(layers=args.layers)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    print(f"[bench] generating {wl.name} inputs on device", file=sys.stderr, flush=True)
+    t0 = time.time()
+    data = device_tensors(wl, device="cuda")
+    torch.cuda.synchronize()
+    print(f"[bench] inputs ready in {time.time() - t0:.1f} s, "
+          f"{torch.cuda.memory_allocated() / 2**30:.1f} GiB", file=sys.stderr, flush=True)
+
+    L, H, G, d, n_c = wl.layers, wl.heads, wl.group, wl.head_dim, wl.n_ctx
+    chunks = wl.chunks()
+    n_heads = L * H
+    K = kvz.kvz_keep_count(n_heads * n_c, wl.keep_ratio)
+    dt_code = 0 if wl.dtype == "bf16" else 1
+    n_in_max = wl.n_prompt + max(m for _, m in chunks)
+    ws_score = torch.empty(kvz.kvz_score_chunk_workspace(dt_code, H, G, n_in_max, d, n_c),
+                           dtype=torch.uint8, device=dev)
+    ws_sel = torch.empty(kvz.kvz_select_workspace(n_heads, n_c), dtype=torch.uint8, device=dev)
+    per_layer_compact = wl.name.startswith("gemma")
+    cmp_heads = H if per_layer_compact else n_heads
+    ws_cmp = torch.empty(kvz.kvz_compact_workspace(cmp_heads, n_c), dtype=torch.uint8, device=dev)
+    S = torch.zeros(n_heads, n_c, dtype=torch.float32, device=dev)
+    mask = torch.empty(n_heads * n_c, dtype=torch.uint8, device=dev)
+    offs = torch.empty(n_heads + 1, dtype=torch.int64, device=dev)
+    tau = torch.empty(1, dtype=torch.float32, device=dev)
+    tdt = data["kc"].dtype
+    k_out = torch.empty(K, d, dtype=tdt, device=dev)
+    v_out = torch.empty(K, d, dtype=tdt, device=dev)
+    idx = torch.empty(K, dtype=torch.int32, device=dev)
+    kc_flat = data["kc"].view(n_heads, n_c, d)
+    vc_flat = data["vc"].view(n_heads, n_c, d)
+    scale = 1 / math.sqrt(d)
+    stream = torch.cuda.current_stream()
+
+    def step():
+        S.zero_()
+        for l in range(L):
+            Sl = S[l * H:(l + 1) * H]
+            for k in range(len(chunks)):
+                kvz.kvz_score_chunk(data["q"][l][k], data["kc"][l], data["kin"][l][k], Sl,
+                                    wl.n_prompt, scale, ws=ws_score, stream=stream)
+        kvz.kvz_select_threshold(S, K, mask, offs, tau, ws=ws_sel, stream=stream)
+        if per_layer_compact:
+            for l in range(L):
+                kvz.kvz_compact(kc_flat[l * H:(l + 1) * H], vc_flat[l * H:(l + 1) * H], mask,
+                                offs, k_out, v_out, idx, head_begin=l * H, ws=ws_cmp,
+                                stream=stream)
+        else:
+            kvz.kvz_compact(kc_flat, vc_flat, mask, offs, k_out, v_out, idx, ws=ws_cmp,
+                            stream=stream)
+
+    for w in range(args.warmup):
+        step()
+        torch.cuda.synchronize()
+        print(f"[bench] warmup step {w} done", file=sys.stderr, flush=True)
+
+    launches_per_step = L * len(chunks) * 3 + 16 + (3 * L if per_layer_compact else 3)
+    kvz.kvz_prof_enable(True, launches_per_step * args.steps + 64)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        step()
+        torch.cuda.synchronize()
+        print(f"[bench] step {s} done at {time.perf_counter() - t0:.2f} s", file=sys.stderr,
+              flush=True)
+    t1 = time.perf_counter()
+    ms_per_step = (t1 - t0) * 1000.0 / args.steps
+
+    names = ["score_pass1", "score_combine", "score_pass2", "select_init", "select_hist",
+             "select_pick", "select_tile_count", "select_scan", "select_mask", "compact_count",
+             "compact_scan", "compact_scatter"]
+    kern = {}
+    for nm in names:
+        n, ms = kvz.kvz_prof_read(nm)
+        if n:
+            kern[nm] = {"launches": n, "total_ms_per_step": ms / args.steps, "avg_us": ms / n * 1e3}
+    kvz.kvz_prof_enable(False)
+
+    # roofline of the dominant kernel (score passes: MFMA-bound)
+    dom = max(kern, key=lambda k: kern[k]["total_ms_per_step"])
+    full = [c for c in chunks if c[1] == wl.chunk]
+    n_in = wl.n_prompt + (full[0][1] if full else chunks[0][1])
+    p1, p2 = score_flops(wl, n_in)
+    roof = None
+    if dom in ("score_pass1", "score_pass2"):
+        # per-launch figure for the full-length chunk; the ragged tail chunk
+        # (if any) is counted by its own flops in the time-weighted average
+        tot_flops = 0.0
+        for (_, m) in chunks:
+            a, b = score_flops(wl, wl.n_prompt + m)
+            tot_flops += a if dom == "score_pass1" else b
+        tot_flops *= L
+        ach = tot_flops / (kern[dom]["total_ms_per_step"] * 1e-3) / 1e12
+        roof = {"bound": "mfma", "achieved": round(ach, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(ach / MFMA_BF16_PEAK_TFLOPS, 4),
+                "traffic": None, "kernel": dom,
+                "flops_per_launch": p1 if dom == "score_pass1" else p2,
+                "avg_launch_us": round(kern[dom]["avg_us"], 2)}
+    # whole-score MFMA fraction over both passes (algorithmic flops)
+    score_ms = sum(kern.get(k, {}).get("total_ms_per_step", 0.0)
+                   for k in ("score_pass1", "score_combine", "score_pass2"))
+    alg = 0.0
+    for (_, m) in chunks:
+        a, b = score_flops(wl, wl.n_prompt + m)
+        alg += a + b
+    alg *= L
+    score_frac = alg / (score_ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS if score_ms else None
+
+    out = {
+        "metric": METRIC,
+        "value": round(n_c / (ms_per_step * 1e-3), 2),
+        "unit": "context tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": wl.dtype,
+        "data": "synthetic",
+        "config": {"workload": wl.name, "layers": L, "kv_heads": H, "group": G, "head_dim": d,
+                   "n_ctx": n_c, "chunk": wl.chunk, "n_prompt": wl.n_prompt,
+                   "keep_ratio": wl.keep_ratio, "keep_count": K},
+        "roofline": roof,
+        "score_mfma_frac": round(score_frac, 4) if score_frac else None,
+        "head_token_scores_per_s": round(n_heads * n_c / (ms_per_step * 1e-3), 1),
+        "kernels": {k: {kk: round(vv, 3) if isinstance(vv, float) else vv for kk, vv in v.items()}
+                    for k, v in kern.items()},
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] timing the CPU oracle on a bounded sample", file=sys.stderr, flush=True)
+        out["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
+    else:
+        out["cpu_baseline"] = None
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,171 @@
+/*
+ * kvz.h -- C ABI of libkvz: KVzip reconstruction-attention scoring, global
+ * keep-ratio selection and compaction of a KV cache on AMD Instinct MI355X
+ * (gfx950).
+ *
+ * The method (sources are named by page title and section):
+ *   - "KVzip: Query-Agnostic KV Cache Compression with Context
+ *     Reconstruction" (jjl357 blog post), section 4.1: prefill the context,
+ *     run a teacher-forced reconstruction (repeat prompt + context), score
+ *     every cached KV pair, sort by score and evict;
+ *     section 4.3.1: the reconstruction attention is a softmax over the
+ *     query-key products of each layer l and KV head h;
+ *     section 4.3.2: the importance of context token j is the maximum, over
+ *     the G query heads of the group and all query rows i, of the normalised
+ *     probability it receives;
+ *     section 4.5.1: the reconstruction runs chunk by chunk and per-chunk
+ *     scores are merged (here: a running max).
+ *   - paperhub.cn OpenReview rebuttals by the authors, answer on positional
+ *     OOD: each chunk's positions continue after the whole prefilled context,
+ *     i.e. every chunk attends to all n_c cached keys; answer on head-level
+ *     scores: the score tensor has shape L x H x n_c.
+ *   - atlas.scime.ai summary, "Approach": the lowest-scoring pairs are
+ *     evicted once per context; "Measured effects": non-uniform KV-head
+ *     budgets.
+ *
+ * Conventions shared by every call
+ *   - Buffers are caller-owned, contiguous, row-major.  Pointers named
+ *     "device" point to device memory on the current HIP device; "host"
+ *     pointers to host memory.  The library allocates no memory: scratch is
+ *     the caller's workspace, sized by the matching *_workspace() query.
+ *   - Every launching call is asynchronous on `stream` (a hipStream_t; NULL
+ *     is the null stream).  Arguments are validated before any launch; on a
+ *     validation error nothing is launched and nothing is written.  Faults of
+ *     launched kernels surface at the caller's next synchronisation.
+ *   - bf16 tensors are raw 16-bit bfloat16 patterns; their pointers must be
+ *     16-byte aligned.  fp32 tensors must be 16-byte aligned as well.
+ *   - The library keeps no state between calls except the optional profiler
+ *     below; calls on different streams may run concurrently if their
+ *     buffers and workspaces are disjoint.
+ */
+#ifndef KVZ_H_
+#define KVZ_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define KVZ_API __attribute__((visibility("default")))
+
+typedef enum {
+  KVZ_OK = 0,
+  KVZ_ERR_INVALID_ARG = 1,     /* null pointer, bad size, misalignment      */
+  KVZ_ERR_UNSUPPORTED = 2,     /* head_dim not in {64,128,256}, bad dtype   */
+  KVZ_ERR_WORKSPACE = 3,       /* workspace smaller than the query returns  */
+  KVZ_ERR_HIP = 4              /* a HIP launch or runtime call failed       */
+} kvz_status;
+
+typedef enum {
+  KVZ_BF16 = 0,                /* bfloat16 inputs, fp32 accumulation        */
+  KVZ_F32 = 1                  /* fp32 inputs, fp32 arithmetic              */
+} kvz_dtype;
+
+/* Human-readable name of a status code (static string, never NULL). */
+KVZ_API const char* kvz_status_string(kvz_status s);
+
+/* ------------------------------------------------------------------------
+ * Scoring of one reconstruction chunk for all KV heads of one layer
+ * (blog 4.3.1, 4.3.2, 4.5.1; rebuttal, positional OOD).
+ *
+ * Shapes (all device, row-major):
+ *   q      [H][G][n_in][d]   query rows of the chunk: rows 0..n_prompt-1 are
+ *                            the repeat prompt, rows n_prompt..n_in-1 the
+ *                            copied context tokens.
+ *   k_ctx  [H][n_c][d]       the layer's cached context keys.
+ *   k_in   [H][n_in][d]      keys of the chunk's own tokens (prompt + copy).
+ *   S      [H][n_c] fp32     running scores, read and written in place.
+ *
+ * For every head h, query head g and row i, the visible keys are all n_c
+ * context keys followed by in-chunk keys 0..i (one causal mask over the
+ * n_in chunk tokens).  With p = softmax(scale * q . k) over those keys,
+ *     S[h][j] <- max(S[h][j], max over g, i of p[j])   for 0 <= j < n_c.
+ * The caller zero-fills S once before the first chunk of a context; the
+ * result does not depend on the order in which chunks are scored.
+ * `scale` (normally 1/sqrt(d)) multiplies the fp32 dot product; it must be
+ * finite and > 0.  n_prompt is validated (0 <= n_prompt <= n_in) and only
+ * documents the row split: every row is a query and is masked the same way.
+ *
+ * Limits: d in {64, 128, 256}; 1 <= n_in, 1 <= n_c <= 2^24, 1 <= H, 1 <= G,
+ * G * n_in <= 2^20.  Workspace: kvz_score_chunk_workspace() bytes, 256-byte
+ * aligned, device memory.
+ * ---------------------------------------------------------------------- */
+KVZ_API size_t kvz_score_chunk_workspace(kvz_dtype dt, int H, int G, int n_in, int d, int n_c);
+
+KVZ_API kvz_status kvz_score_chunk(kvz_dtype dt, int H, int G, int d, int n_c, int n_prompt,
+                           int n_in, const void* q, const void* k_ctx, const void* k_in,
+                           float scale, float* S, void* ws, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
+ * Keep count K = r * N rounded half up, clamped to [0, N] (host only).
+ * ---------------------------------------------------------------------- */
+KVZ_API int64_t kvz_keep_count(int64_t N, double r);
+
+/* ------------------------------------------------------------------------
+ * Global selection over every (layer, head, token) score (blog 4.1 step 5;
+ * atlas, Approach and Measured effects).
+ *
+ *   S            device fp32 [n_heads][n_c], n_heads = L*H in flat (l, h)
+ *                order; every score must be >= 0 and not NaN (scores from
+ *                kvz_score_chunk are).
+ *   K            number of entries to keep, 0 <= K <= n_heads * n_c.
+ *   mask         device uint8 [n_heads * n_c], out: 1 = kept.
+ *   head_offsets device int64 [n_heads + 1], out: head_offsets[0] = 0 and
+ *                head_offsets[h+1] - head_offsets[h] = kept count of head h.
+ *   tau_out      device fp32 [1], out: the K-th largest score (+inf if K=0).
+ *
+ * Exactly K entries are kept: every score > tau, then the scores equal to tau
+ * in ascending flat index (l*H + h)*n_c + j until K is reached.  No
+ * device-to-host synchronisation happens.
+ * Limits: n_heads * n_c < 2^31.  Workspace: kvz_select_workspace() bytes.
+ * ---------------------------------------------------------------------- */
+KVZ_API size_t kvz_select_workspace(int64_t n_heads, int n_c);
+
+KVZ_API kvz_status kvz_select_threshold(const float* S, int64_t n_heads, int n_c, int64_t K,
+                                uint8_t* mask, int64_t* head_offsets, float* tau_out,
+                                void* ws, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
+ * Compaction of the kept rows into a packed per-head cache (blog 4.1 step 5;
+ * rebuttal, the compressed cache is built once and reused by many queries).
+ *
+ * Packs heads [head_begin, head_begin + head_count) so that a whole cache
+ * can be packed in one call or one layer at a time.
+ *   k_ctx, v_ctx  device [head_count][n_c][d] rows of those heads (pointer to
+ *                 head head_begin), element type dt.
+ *   mask          device uint8 [n_heads * n_c], the full mask from
+ *                 kvz_select_threshold (indexed by absolute head).
+ *   head_offsets  device int64 [n_heads + 1] from kvz_select_threshold.
+ *   k_out, v_out  device [K][d] packed outputs, idx_out device int32 [K]:
+ *                 for absolute head h, the r-th kept j (ascending) goes to
+ *                 row head_offsets[h] + r, with idx_out = j.
+ * Rows are copied bit-exactly.  Workspace: kvz_compact_workspace() bytes.
+ * Limits: d in {64, 128, 256}.
+ * ---------------------------------------------------------------------- */
+KVZ_API size_t kvz_compact_workspace(int64_t head_count, int n_c);
+
+KVZ_API kvz_status kvz_compact(kvz_dtype dt, int d, int n_c, int64_t head_begin, int64_t head_count,
+                       const void* k_ctx, const void* v_ctx, const uint8_t* mask,
+                       const int64_t* head_offsets, void* k_out, void* v_out,
+                       int32_t* idx_out, void* ws, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
+ * Optional kernel timer (measurement only; not thread-safe).
+ * While enabled, every kernel the library launches is bracketed by a pair of
+ * HIP events on its stream.  kvz_prof_read() synchronises those events and
+ * returns, for the kernel named `name` ("score_pass1", "score_combine",
+ * "score_pass2", "select_*", "compact_*"), the number of launches and the
+ * summed duration in milliseconds since the last enable.  Returns KVZ_OK, or
+ * KVZ_ERR_INVALID_ARG for an unknown name.  max_launches bounds the event
+ * pool; launches beyond it are not timed.
+ * ---------------------------------------------------------------------- */
+KVZ_API kvz_status kvz_prof_enable(int on, int max_launches);
+KVZ_API kvz_status kvz_prof_read(const char* name, int64_t* launches, double* total_ms);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KVZ_H_ */
