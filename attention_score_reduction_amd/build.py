@@ -17,6 +17,8 @@ FLAGS = [
     # no packed-fp32 instructions in any device code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-fvisibility=hidden",
+    # MFMA accumulators in VGPRs (no AGPR copies before the softmax VALU work)
+    "-mllvm", "-amdgpu-mfma-vgpr-form=1",
 ]
 
 

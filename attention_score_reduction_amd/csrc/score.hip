@@ -56,9 +56,10 @@ __device__ __forceinline__ void online_update(const f32x16& a, float& m, float& 
 #pragma unroll
   for (int v = 1; v < 16; ++v) mx = fmaxf(mx, a[v]);
   const float mn = fmaxf(m, mx * cl2);
-  float s0 = 0.f, s1 = 0.f, s2 = 0.f, s3 = 0.f;
+  float s0 = fast_exp2(fmaf(a[0], cl2, -mn)), s1 = fast_exp2(fmaf(a[1], cl2, -mn));
+  float s2 = fast_exp2(fmaf(a[2], cl2, -mn)), s3 = fast_exp2(fmaf(a[3], cl2, -mn));
 #pragma unroll
-  for (int v = 0; v < 16; v += 4) {
+  for (int v = 4; v < 16; v += 4) {
     s0 += fast_exp2(fmaf(a[v + 0], cl2, -mn));
     s1 += fast_exp2(fmaf(a[v + 1], cl2, -mn));
     s2 += fast_exp2(fmaf(a[v + 2], cl2, -mn));
@@ -116,13 +117,14 @@ __global__ __launch_bounds__(256) void score_pass1_bf16(
 
   // stationary query operand (B of K*Q^T): this lane's query column n
   bf16x8 qr[2][KS];
-  int irow[2];
+  int irow[2], grow[2];
 #pragma unroll
   for (int t = 0; t < 2; ++t) {
     const int r = rt * P1_ROWS + wave * 64 + t * 32 + n;
     irow[t] = r / G;
+    grow[t] = r - irow[t] * G;
     if (r < R) {
-      const int g = r - irow[t] * G;
+      const int g = grow[t];
       const uint16_t* p = q + ((size_t)(h * G + g) * n_in + irow[t]) * D + half * 8;
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) qr[t][ks] = as_bf16x8(ld16(p + ks * 16));
@@ -195,9 +197,10 @@ __global__ __launch_bounds__(256) void score_pass1_bf16(
     const float lo = __shfl_xor(l[t], 32);
     const float M = fmaxf(m[t], mo);
     const float L = l[t] * fast_exp2(m[t] - M) + lo * fast_exp2(mo - M);
-    if (half == 0) {
-      const int r = rt * P1_ROWS + wave * 64 + t * 32 + n;
-      part[((size_t)h * splits + s) * R_pad + r] = make_float2(M, L);
+    const int r = rt * P1_ROWS + wave * 64 + t * 32 + n;
+    if (half == 0 && r < R) {
+      // partials and lse are stored in g-major row order (g * n_in + i)
+      part[((size_t)h * splits + s) * R_pad + grow[t] * n_in + irow[t]] = make_float2(M, L);
     }
   }
 }
@@ -263,6 +266,7 @@ __global__ __launch_bounds__(256) void score_pass2_bf16(
   }
 
   const float* lseh = lse2 + (size_t)h * R_pad;
+  const uint16_t* qh = q + (size_t)h * R * D;  // rows of head h, g-major: g * n_in + i
   const int n_stages = R_pad / P2_RS;
   uint4 reg[LOADS];
   float4 lreg = make_float4(0.f, 0.f, 0.f, 0.f);
@@ -272,8 +276,7 @@ __global__ __launch_bounds__(256) void score_pass2_bf16(
     for (int u = 0; u < LOADS; ++u) {
       const int c = tid + 256 * u, row = c / CH, ch = c % CH, r = r0 + row;
       if (r < R) {
-        const int i = r / G, g = r - i * G;
-        reg[u] = ld16(q + ((size_t)(h * G + g) * n_in + i) * D + ch * 8);
+        reg[u] = ld16(qh + (size_t)r * D + ch * 8);
       } else {
         reg[u] = make_uint4(0, 0, 0, 0);
       }
