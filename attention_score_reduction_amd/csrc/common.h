@@ -4,7 +4,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
-#include "../../include/kvz.h"
+#include "kvz.h"
 
 namespace kvz {
 

@@ -35,8 +35,11 @@ namespace {
 constexpr int KT = 32;          // keys per pass-1 tile
 constexpr int P1_ROWS = 256;    // query rows per pass-1 workgroup (4 waves x 64)
 constexpr int P2_KEYS = 256;    // context keys per pass-2 workgroup (4 waves x 64)
-constexpr int P2_RS = 64;       // query rows per pass-2 LDS stage
 constexpr float kNegBig = -1e30f;
+
+#ifndef KVZ_P1_TARGET_WGS
+#define KVZ_P1_TARGET_WGS 4096  // pass-1 workgroups aimed for per call (sets the key splits)
+#endif
 
 template <int D>
 struct Geo {
@@ -50,7 +53,11 @@ __device__ __forceinline__ int swz(int row, int ch) {
   return row * CH + (ch ^ (row & SWZ));
 }
 
-// Online max/sum of 16 logits (raw dot products) into (m, l), log2 domain.
+// scheduling-group masks of __builtin_amdgcn_sched_group_barrier
+constexpr int SG_VALU = 0x002, SG_MFMA = 0x008, SG_VMEM_READ = 0x020, SG_DS_READ = 0x100;
+
+// Exact online max/sum of 16 logits (raw dot products) into (m, l), log2
+// domain: raise m to the tile max, rescale l, add the tile's terms.
 __device__ __forceinline__ void online_update(const f32x16& a, float& m, float& l, float cl2) {
   float mx = a[0];
 #pragma unroll
@@ -69,6 +76,35 @@ __device__ __forceinline__ void online_update(const f32x16& a, float& m, float& 
   m = mn;
 }
 
+// Sum of 2^(x*cl2 - m) over 16 logits against a fixed (possibly stale) m.
+// Lazy rescaling: the running max only moves when a tile's sum exceeds
+// kLazyLimit (or is inf/NaN-free but huge), which bounds every term by 2^30
+// relative to m; the common tile then costs one fma, one exp and one add per
+// logit instead of an extra max.  l stays below 2^30 * tiles, far from fp32
+// overflow, and m - log2(l) is unchanged by the choice of m.
+constexpr float kLazyLimit = 1073741824.f;  // 2^30
+
+__device__ __forceinline__ float tile_sum(const f32x16& a, float m, float cl2) {
+  float e[16];
+#pragma unroll
+  for (int v = 0; v < 16; ++v) e[v] = fast_exp2(fmaf(a[v], cl2, -m));
+  return (((e[0] + e[1]) + (e[2] + e[3])) + ((e[4] + e[5]) + (e[6] + e[7]))) +
+         (((e[8] + e[9]) + (e[10] + e[11])) + ((e[12] + e[13]) + (e[14] + e[15])));
+}
+
+// Commit the sums of both query columns of a lane; one branch for both so
+// that the two sums are computed before it (and overlap the MFMAs).
+__device__ __forceinline__ void lazy_commit2(const f32x16 (&a)[2], float s0, float s1,
+                                             float (&m)[2], float (&l)[2], float cl2) {
+  if (fmaxf(s0, s1) <= kLazyLimit) {
+    l[0] += s0;
+    l[1] += s1;
+  } else {
+    if (s0 <= kLazyLimit) l[0] += s0; else online_update(a[0], m[0], l[0], cl2);
+    if (s1 <= kLazyLimit) l[1] += s1; else online_update(a[1], m[1], l[1], cl2);
+  }
+}
+
 // Row index (within a 32x32 MFMA output tile) held by accumulator v of a lane.
 __device__ __forceinline__ int acc_row(int v, int half) {
   return 8 * (v >> 2) + 4 * half + (v & 3);
@@ -77,6 +113,14 @@ __device__ __forceinline__ int acc_row(int v, int half) {
 // ---------------------------------------------------------------------------
 // pass 1, bf16: partial (max, sum) per query row and key split
 // grid: H x splits x row-tiles (XCD-remapped: head-major, row tile fastest)
+//
+// Main loop (tiles with no masked key): software-pipelined over 32-key
+// tiles.  Iteration t prefetches tile t+2 from global memory into registers,
+// issues the LDS reads and MFMAs of tile t+1 into one accumulator set and,
+// interleaved with them, the exp/sum work of tile t from the other set; it
+// then stores tile t+2 into the LDS buffer that tile t occupied.  One barrier
+// per tile.  Masked tiles (the ragged last context tile, the causal in-chunk
+// keys) take a simple unpipelined path.
 // ---------------------------------------------------------------------------
 template <int D>
 __global__ __launch_bounds__(256) void score_pass1_bf16(
@@ -99,20 +143,22 @@ __global__ __launch_bounds__(256) void score_pass1_bf16(
   const int n = lane & 31, half = lane >> 5;
 
   const bool inchunk = (s == n_split_ctx);
+  const int n_tiles_ctx = (n_c + KT - 1) / KT;
   const uint16_t* kbase;
-  int nkeys, t_begin, t_end;
+  int nkeys, t_begin, t_end, t_clean;
   if (!inchunk) {
     kbase = kc + (size_t)h * n_c * D;
     nkeys = n_c;
-    const int n_tiles_ctx = (n_c + KT - 1) / KT;
     t_begin = s * tiles_per_split;
     t_end = min(n_tiles_ctx, t_begin + tiles_per_split);
+    t_clean = (t_end == n_tiles_ctx && (n_c % KT) != 0) ? t_end - 1 : t_end;
   } else {
     kbase = kin + (size_t)h * n_in * D;
     nkeys = n_in;
     const int rlast = min(R, (rt + 1) * P1_ROWS) - 1;
     t_begin = 0;
     t_end = (rlast / G) / KT + 1;
+    t_clean = t_begin;  // every in-chunk tile is causally masked
   }
 
   // stationary query operand (B of K*Q^T): this lane's query column n
@@ -124,8 +170,7 @@ __global__ __launch_bounds__(256) void score_pass1_bf16(
     irow[t] = r / G;
     grow[t] = r - irow[t] * G;
     if (r < R) {
-      const int g = grow[t];
-      const uint16_t* p = q + ((size_t)(h * G + g) * n_in + irow[t]) * D + half * 8;
+      const uint16_t* p = q + ((size_t)(h * G + grow[t]) * n_in + irow[t]) * D + half * 8;
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) qr[t][ks] = as_bf16x8(ld16(p + ks * 16));
     } else {
@@ -135,59 +180,132 @@ __global__ __launch_bounds__(256) void score_pass1_bf16(
   }
 
   float m[2] = {kNegBig, kNegBig}, l[2] = {0.f, 0.f};
+  uint4 reg[LOADS];
+  auto load_tile = [&](int tile) {
+#pragma unroll
+    for (int u = 0; u < LOADS; ++u) {
+      const int c = tid + 256 * u, row = c / CH, ch = c % CH, key = tile * KT + row;
+      reg[u] = key < nkeys ? ld16(kbase + (size_t)key * D + ch * 8) : make_uint4(0, 0, 0, 0);
+    }
+  };
+  auto store_tile = [&](int buf) {
+#pragma unroll
+    for (int u = 0; u < LOADS; ++u) {
+      const int c = tid + 256 * u, row = c / CH, ch = c % CH;
+      lds[buf][swz<CH, SWZ>(row, ch)] = reg[u];
+    }
+  };
+  // tiles of the clean range hold KT valid keys: no bounds test, no branch
+  auto load_full = [&](int tile, uint4 (&r)[LOADS]) {
+#pragma unroll
+    for (int u = 0; u < LOADS; ++u) {
+      const int c = tid + 256 * u, row = c / CH, ch = c % CH, key = tile * KT + row;
+      r[u] = ld16(kbase + (size_t)key * D + ch * 8);
+    }
+  };
+  auto store_regs = [&](int buf, const uint4 (&r)[LOADS]) {
+#pragma unroll
+    for (int u = 0; u < LOADS; ++u) {
+      const int c = tid + 256 * u, row = c / CH, ch = c % CH;
+      lds[buf][swz<CH, SWZ>(row, ch)] = r[u];
+    }
+  };
+  auto mfma_tile = [&](int buf, f32x16 (&c)[2]) {
+    bf16x8 a[KS];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) a[ks] = as_bf16x8(lds[buf][swz<CH, SWZ>(n, ks * 2 + half)]);
+    const f32x16 z = {};
+    c[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[0], qr[0][0], z, 0, 0, 0);
+    c[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[0], qr[1][0], z, 0, 0, 0);
+#pragma unroll
+    for (int ks = 1; ks < KS; ++ks) {
+      c[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[ks], qr[0][ks], c[0], 0, 0, 0);
+      c[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[ks], qr[1][ks], c[1], 0, 0, 0);
+    }
+  };
 
-  if (t_begin < t_end) {
-    uint4 reg[LOADS];
-    auto load_tile = [&](int tile) {
+  const int nclean = t_clean - t_begin;
+  if (nclean > 0) {
+    // Tile t lives in LDS buffer t & 1.  Iteration it: global loads of tile
+    // it+2, then 2*KS MFMAs of tile it+1, each preceded by an equal share of
+    // the exp/sum work of tile it (explicit order, fenced against the
+    // scheduler), then the LDS store of tile it+2 and one barrier.  Indices
+    // past the range re-load the last tile; those copies are never consumed.
+    constexpr int NCH = 2 * KS;      // one chunk of VALU work per MFMA
+    constexpr int PER = 32 / NCH;    // logits per chunk (2 columns x 16)
+    f32x16 A[2], B[2];
+    const int last = nclean - 1;
+    load_full(t_begin, reg);
+    store_regs(0, reg);
+    __syncthreads();
+    load_full(t_begin + min(1, last), reg);
+    mfma_tile(0, A);
+    store_regs(1, reg);
+    __syncthreads();
+    auto body = [&](int it, f32x16 (&cur)[2], f32x16 (&nxt)[2]) {
+      load_full(t_begin + min(it + 2, last), reg);
+      const int buf = (it + 1) & 1;
+      bf16x8 a[KS];
 #pragma unroll
-      for (int u = 0; u < LOADS; ++u) {
-        const int c = tid + 256 * u, row = c / CH, ch = c % CH, key = tile * KT + row;
-        reg[u] = key < nkeys ? ld16(kbase + (size_t)key * D + ch * 8) : make_uint4(0, 0, 0, 0);
-      }
-    };
-    auto store_tile = [&](int buf) {
+      for (int ks = 0; ks < KS; ++ks)
+        a[ks] = as_bf16x8(lds[buf][swz<CH, SWZ>(n, ks * 2 + half)]);
+      __builtin_amdgcn_sched_barrier(0);
+      const f32x16 z = {};
+      float sm[2][4];
 #pragma unroll
-      for (int u = 0; u < LOADS; ++u) {
-        const int c = tid + 256 * u, row = c / CH, ch = c % CH;
-        lds[buf][swz<CH, SWZ>(row, ch)] = reg[u];
+      for (int c = 0; c < NCH; ++c) {
+#pragma unroll
+        for (int e = c * PER; e < (c + 1) * PER; ++e) {
+          const int col = e >> 4, v = e & 15;
+          const float x = fast_exp2(fmaf(cur[col][v], cl2, -m[col]));
+          if (v < 4) sm[col][v] = x; else sm[col][v & 3] += x;
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        const int ks = c >> 1, t = c & 1;
+        nxt[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[ks], qr[t][ks], ks == 0 ? z : nxt[t],
+                                                         0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
       }
+      const float s0 = (sm[0][0] + sm[0][1]) + (sm[0][2] + sm[0][3]);
+      const float s1 = (sm[1][0] + sm[1][1]) + (sm[1][2] + sm[1][3]);
+      lazy_commit2(cur, s0, s1, m, l, cl2);
+      store_regs(it & 1, reg);
+      __syncthreads();
     };
-    load_tile(t_begin);
+    auto finish = [&](f32x16 (&cur)[2]) {
+      lazy_commit2(cur, tile_sum(cur[0], m[0], cl2), tile_sum(cur[1], m[1], cl2), m, l, cl2);
+    };
+    int it = 0;
+    for (; it + 2 < nclean; it += 2) {
+      body(it, A, B);
+      body(it + 1, B, A);
+    }
+    if (it + 1 < nclean) {
+      body(it, A, B);
+      finish(B);
+    } else {
+      finish(A);
+    }
+  }
+
+  // masked tiles: ragged context tail or causal in-chunk keys
+  for (int tile = t_clean; tile < t_end; ++tile) {
+    __syncthreads();
+    load_tile(tile);
     store_tile(0);
     __syncthreads();
-    for (int it = t_begin; it < t_end; ++it) {
-      const int buf = (it - t_begin) & 1;
-      const bool more = it + 1 < t_end;
-      if (more) load_tile(it + 1);
-      f32x16 acc0 = {}, acc1 = {};
+    f32x16 c[2];
+    mfma_tile(0, c);
+    const int key0 = tile * KT;
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        const bf16x8 a = as_bf16x8(lds[buf][swz<CH, SWZ>(n, ks * 2 + half)]);
-        acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qr[0][ks], acc0, 0, 0, 0);
-        acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qr[1][ks], acc1, 0, 0, 0);
-      }
-      const int key0 = it * KT;
-      if (inchunk) {
-#pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const int key = key0 + acc_row(v, half);
-          if (key > irow[0]) acc0[v] = -INFINITY;
-          if (key > irow[1]) acc1[v] = -INFINITY;
-        }
-      } else if (key0 + KT > n_c) {
-#pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          if (key0 + acc_row(v, half) >= n_c) {
-            acc0[v] = -INFINITY;
-            acc1[v] = -INFINITY;
-          }
-        }
-      }
-      online_update(acc0, m[0], l[0], cl2);
-      online_update(acc1, m[1], l[1], cl2);
-      if (more) store_tile(buf ^ 1);
-      __syncthreads();
+    for (int v = 0; v < 16; ++v) {
+      const int key = key0 + acc_row(v, half);
+      const bool bad = inchunk ? false : key >= n_c;
+      if (bad || (inchunk && key > irow[0])) c[0][v] = -INFINITY;
+      if (bad || (inchunk && key > irow[1])) c[1][v] = -INFINITY;
     }
+    online_update(c[0], m[0], l[0], cl2);
+    online_update(c[1], m[1], l[1], cl2);
   }
 
   // lanes n and n+32 hold the same query column, different key rows
@@ -231,6 +349,11 @@ __global__ __launch_bounds__(256) void score_combine(const float2* __restrict__ 
 // ---------------------------------------------------------------------------
 // pass 2, bf16: column max over all query rows, running max into S
 // grid: H x key-tiles of 256 (XCD-remapped: head-major)
+//
+// Same pipeline as pass 1 with the roles swapped: each wave keeps 64 context
+// keys in registers and sweeps 32-row query tiles staged in LDS; iteration t
+// issues the MFMAs of row tile t+1 interleaved with the fma/max epilogue of
+// tile t, whose lse values were prefetched one iteration earlier.
 // ---------------------------------------------------------------------------
 template <int D>
 __global__ __launch_bounds__(256) void score_pass2_bf16(
@@ -238,9 +361,9 @@ __global__ __launch_bounds__(256) void score_pass2_bf16(
     const float* __restrict__ lse2, float* __restrict__ S, int G, int n_c, int n_in, int R,
     int R_pad, int n_kt, float cl2, int n_blocks) {
   constexpr int KS = Geo<D>::KS, CH = Geo<D>::CH, SWZ = Geo<D>::SWZ;
-  constexpr int LOADS = P2_RS * CH / 256;
-  __shared__ uint4 ldq[2][P2_RS * CH];
-  __shared__ float4 ldl[2][P2_RS / 4];
+  constexpr int RT = 32;                     // query rows per tile
+  constexpr int LOADS = RT * CH / 256;
+  __shared__ uint4 ldq[2][RT * CH];
 
   const int lb = xcd_logical_block();
   if (lb >= n_blocks) return;
@@ -267,63 +390,113 @@ __global__ __launch_bounds__(256) void score_pass2_bf16(
 
   const float* lseh = lse2 + (size_t)h * R_pad;
   const uint16_t* qh = q + (size_t)h * R * D;  // rows of head h, g-major: g * n_in + i
-  const int n_stages = R_pad / P2_RS;
+  const int n_tiles = R_pad / RT;
+  const int last = n_tiles - 1;
   uint4 reg[LOADS];
-  float4 lreg = make_float4(0.f, 0.f, 0.f, 0.f);
-  auto load_stage = [&](int st) {
-    const int r0 = st * P2_RS;
+  auto load_tile = [&](int t) {
 #pragma unroll
     for (int u = 0; u < LOADS; ++u) {
-      const int c = tid + 256 * u, row = c / CH, ch = c % CH, r = r0 + row;
-      if (r < R) {
-        reg[u] = ld16(qh + (size_t)r * D + ch * 8);
-      } else {
-        reg[u] = make_uint4(0, 0, 0, 0);
-      }
+      // padding rows (r >= R) re-read row R-1; their lse is +inf, so they
+      // never win the max and need no zero fill (and no branch)
+      const int c = tid + 256 * u, row = c / CH, ch = c % CH, rr = min(t * RT + row, R - 1);
+      reg[u] = ld16(qh + (size_t)rr * D + ch * 8);
     }
-    if (tid < P2_RS / 4) lreg = reinterpret_cast<const float4*>(lseh + r0)[tid];
   };
-  auto store_stage = [&](int buf) {
+  auto store_tile = [&](int buf) {
 #pragma unroll
     for (int u = 0; u < LOADS; ++u) {
       const int c = tid + 256 * u, row = c / CH, ch = c % CH;
       ldq[buf][swz<CH, SWZ>(row, ch)] = reg[u];
     }
-    if (tid < P2_RS / 4) ldl[buf][tid] = lreg;
+  };
+  // lse of the 16 rows this lane holds in the MFMA output of tile t
+  auto load_lse = [&](int t, float4 (&L)[4]) {
+#pragma unroll
+    for (int vg = 0; vg < 4; ++vg)
+      L[vg] = *reinterpret_cast<const float4*>(lseh + t * RT + 8 * vg + 4 * half);
+  };
+  auto mfma_tile = [&](int buf, f32x16 (&c)[2]) {
+    bf16x8 a[KS];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) a[ks] = as_bf16x8(ldq[buf][swz<CH, SWZ>(n, ks * 2 + half)]);
+    const f32x16 z = {};
+    c[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[0], kr[0][0], z, 0, 0, 0);
+    c[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[0], kr[1][0], z, 0, 0, 0);
+#pragma unroll
+    for (int ks = 1; ks < KS; ++ks) {
+      c[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[ks], kr[0][ks], c[0], 0, 0, 0);
+      c[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[ks], kr[1][ks], c[1], 0, 0, 0);
+    }
+  };
+  // two running maxima per column (alternating by element pair) keep the
+  // max chains short; each pair of elements costs two fma and one max3
+  float mx[2][2] = {{-INFINITY, -INFINITY}, {-INFINITY, -INFINITY}};
+  auto lse_of = [](const float4 (&L)[4], int v) {
+    const float4 L4 = L[v >> 2];
+    return (v & 3) == 0 ? L4.x : (v & 3) == 1 ? L4.y : (v & 3) == 2 ? L4.z : L4.w;
+  };
+  // elements e and e+1 (same column, e even)
+  auto epi_pair = [&](const f32x16 (&c)[2], const float4 (&L)[4], int e) {
+    const int col = e >> 4, v = e & 15;
+    const float t0 = fmaf(c[col][v], cl2, -lse_of(L, v));
+    const float t1 = fmaf(c[col][v + 1], cl2, -lse_of(L, v + 1));
+    float& acc = mx[col][(v >> 1) & 1];
+    acc = fmaxf(acc, fmaxf(t0, t1));
   };
 
-  float mx0 = -INFINITY, mx1 = -INFINITY;
-  load_stage(0);
-  store_stage(0);
+  // Tile t lives in LDS buffer t & 1; same schedule as pass 1 with the
+  // fma/max epilogue of tile it spread over the MFMAs of tile it+1.
+  constexpr int NCH = 2 * KS;
+  constexpr int PER = 32 / NCH;
+  f32x16 A[2], B[2];
+  float4 LA[4], LB[4];
+  load_tile(0);
+  store_tile(0);
+  load_lse(0, LA);
   __syncthreads();
-  for (int st = 0; st < n_stages; ++st) {
-    const int buf = st & 1;
-    const bool more = st + 1 < n_stages;
-    if (more) load_stage(st + 1);
+  load_tile(min(1, last));
+  mfma_tile(0, A);
+  store_tile(1);
+  __syncthreads();
+  auto body = [&](int it, f32x16 (&cur)[2], f32x16 (&nxt)[2], const float4 (&Lc)[4],
+                  float4 (&Ln)[4]) {
+    load_tile(min(it + 2, last));
+    load_lse(it + 1, Ln);
+    const int buf = (it + 1) & 1;
+    bf16x8 a[KS];
 #pragma unroll
-    for (int sub = 0; sub < 2; ++sub) {
-      f32x16 acc0 = {}, acc1 = {};
+    for (int ks = 0; ks < KS; ++ks) a[ks] = as_bf16x8(ldq[buf][swz<CH, SWZ>(n, ks * 2 + half)]);
+    __builtin_amdgcn_sched_barrier(0);
+    const f32x16 z = {};
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        const bf16x8 a = as_bf16x8(ldq[buf][swz<CH, SWZ>(sub * 32 + n, ks * 2 + half)]);
-        acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, kr[0][ks], acc0, 0, 0, 0);
-        acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, kr[1][ks], acc1, 0, 0, 0);
-      }
+    for (int c = 0; c < NCH; ++c) {
 #pragma unroll
-      for (int vg = 0; vg < 4; ++vg) {
-        const float4 L4 = ldl[buf][(sub * 32 + 8 * vg + 4 * half) >> 2];
-        const float lv[4] = {L4.x, L4.y, L4.z, L4.w};
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int v = vg * 4 + e;
-          mx0 = fmaxf(mx0, fmaf(acc0[v], cl2, -lv[e]));
-          mx1 = fmaxf(mx1, fmaf(acc1[v], cl2, -lv[e]));
-        }
-      }
+      for (int e = c * PER; e < (c + 1) * PER; e += 2) epi_pair(cur, Lc, e);
+      __builtin_amdgcn_sched_barrier(0);
+      const int ks = c >> 1, t = c & 1;
+      nxt[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[ks], kr[t][ks], ks == 0 ? z : nxt[t],
+                                                       0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
     }
-    if (more) store_stage(buf ^ 1);
+    store_tile(it & 1);
     __syncthreads();
+  };
+  auto finish = [&](const f32x16 (&cur)[2], const float4 (&Lc)[4]) {
+#pragma unroll
+    for (int e = 0; e < 32; e += 2) epi_pair(cur, Lc, e);
+  };
+  int it = 0;
+  for (; it + 2 < n_tiles; it += 2) {
+    body(it, A, B, LA, LB);
+    body(it + 1, B, A, LB, LA);
   }
+  if (it + 1 < n_tiles) {
+    body(it, A, B, LA, LB);
+    finish(B, LB);
+  } else {
+    finish(A, LA);
+  }
+  float mx0 = fmaxf(mx[0][0], mx[0][1]), mx1 = fmaxf(mx[1][0], mx[1][1]);
 
   mx0 = fmaxf(mx0, __shfl_xor(mx0, 32));
   mx1 = fmaxf(mx1, __shfl_xor(mx1, 32));
@@ -476,7 +649,7 @@ ScorePlan score_plan(kvz_dtype dt, int H, int G, int n_in, int d, int n_c) {
   const int n_ctx_tiles = (n_c + KT - 1) / KT;
   if (dt == KVZ_BF16) {
     // enough workgroups to cover the chip a few times, at least 16 tiles each
-    int want = (2048 + H * p.n_rt - 1) / (H * p.n_rt);
+    int want = (KVZ_P1_TARGET_WGS + H * p.n_rt - 1) / (H * p.n_rt);
     int maxs = n_ctx_tiles / 16;
     if (maxs < 1) maxs = 1;
     if (want > maxs) want = maxs;
