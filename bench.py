@@ -35,6 +35,29 @@ def score_flops(wl, n_in):
     return p1, p2
 
 
+def measured_traffic(kernel, workload):
+    """HBM bytes per launch of `kernel` from the committed counter summary
+    (profiles/<kernel>_<workload>_traffic.md), or None when that summary was
+    taken on a different kernel source than the one built now."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_traffic.md")
+    src = os.path.join(ROOT, "attention_score_reduction_amd", "csrc", "score.hip")
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    for line in open(path):
+        if ":" in line and line.startswith("- "):
+            k, v = line[2:].split(":", 1)
+            fields[k.strip()] = v.strip()
+    sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
+    if fields.get("score.hip sha256") != sha:
+        return None
+    try:
+        return int(fields["HBM bytes per launch"])
+    except (KeyError, ValueError):
+        return None
+
+
 def cpu_baseline(wl, budget_s):
     """The oracle as it stands on a bounded sample: one (layer, head) pair,
     as many whole chunks as fit in about budget_s seconds; the full step is
@@ -83,6 +106,9 @@ def main():
     ap.add_argument("--layers", type=int, default=None, help="fewer layers (debug only)")
     ap.add_argument("--cpu-seconds", type=float, default=20.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="after the timed steps, run a 2 GiB device-to-device copy (a plain copy "
+                         "kernel of known size, to scale the HBM traffic counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
@@ -175,6 +201,28 @@ def main():
             kern[nm] = {"launches": n, "total_ms_per_step": ms / args.steps, "avg_us": ms / n * 1e3}
     kvz.kvz_prof_enable(False)
 
+    # HBM-bound kernels: algorithmic bytes per step / their time
+    row_bytes = d * (2 if wl.dtype == "bf16" else 4)
+    N = n_heads * n_c
+    hbm_bytes = {
+        # gather K and V rows, write them packed, idx, read the mask
+        "compact_scatter": K * (4 * row_bytes + 4) + N,
+        # three histogram rounds, tile counts, mask pass (reads of S) + mask write
+        "select_total": 5 * 4 * N + N,
+    }
+    hbm = {}
+    if "compact_scatter" in kern:
+        t = kern["compact_scatter"]["total_ms_per_step"] * 1e-3
+        hbm["compact_scatter"] = {"bytes": hbm_bytes["compact_scatter"],
+                                  "achieved_GBs": round(hbm_bytes["compact_scatter"] / t / 1e9, 1),
+                                  "frac": round(hbm_bytes["compact_scatter"] / t / 1e9 / HBM_PEAK_GBS, 4)}
+    sel_ms = sum(v["total_ms_per_step"] for k2, v in kern.items() if k2.startswith("select_"))
+    if sel_ms:
+        hbm["select_total"] = {"bytes": hbm_bytes["select_total"],
+                               "achieved_GBs": round(hbm_bytes["select_total"] / (sel_ms * 1e-3) / 1e9, 1),
+                               "frac": round(hbm_bytes["select_total"] / (sel_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                               "time_ms": round(sel_ms, 4)}
+
     # roofline of the dominant kernel (score passes: MFMA-bound)
     dom = max(kern, key=lambda k: kern[k]["total_ms_per_step"])
     full = [c for c in chunks if c[1] == wl.chunk]
@@ -192,7 +240,7 @@ def main():
         ach = tot_flops / (kern[dom]["total_ms_per_step"] * 1e-3) / 1e12
         roof = {"bound": "mfma", "achieved": round(ach, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(ach / MFMA_BF16_PEAK_TFLOPS, 4),
-                "traffic": None, "kernel": dom,
+                "traffic": measured_traffic(dom, wl.name), "kernel": dom,
                 "flops_per_launch": p1 if dom == "score_pass1" else p2,
                 "avg_launch_us": round(kern[dom]["avg_us"], 2)}
     # whole-score MFMA fraction over both passes (algorithmic flops)
@@ -223,10 +271,20 @@ def main():
                    "keep_ratio": wl.keep_ratio, "keep_count": K},
         "roofline": roof,
         "score_mfma_frac": round(score_frac, 4) if score_frac else None,
+        "hbm_kernels": hbm,
         "head_token_scores_per_s": round(n_heads * n_c / (ms_per_step * 1e-3), 1),
         "kernels": {k: {kk: round(vv, 3) if isinstance(vv, float) else vv for kk, vv in v.items()}
                     for k, v in kern.items()},
     }
+    if args.copy_calibration:
+        nbytes = 2 << 30
+        src_t = torch.ones(nbytes // 4, dtype=torch.float32, device=dev)
+        dst_t = torch.empty_like(src_t)
+        for _ in range(3):
+            dst_t.copy_(src_t)
+        torch.cuda.synchronize()
+        out["copy_calibration_bytes"] = nbytes
+        del src_t, dst_t
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle on a bounded sample", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
