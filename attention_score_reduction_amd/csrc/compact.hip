@@ -19,6 +19,7 @@ namespace {
 
 constexpr int TILE = 4096;
 constexpr int TPB = 256;
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 constexpr int PER_T = TILE / TPB;
 
 __global__ __launch_bounds__(TPB) void cmp_count(const uint8_t* __restrict__ mask,
@@ -54,11 +55,15 @@ __global__ void cmp_scan(const uint32_t* __restrict__ cnt, const int64_t* __rest
   }
 }
 
+// RC = 16-byte chunks per row (row bytes / 16), a compile-time constant so
+// the (row, chunk) split of the copy index is a shift.
+template <int RC>
 __global__ __launch_bounds__(TPB) void cmp_scatter(
-    const uint4* __restrict__ kc, const uint4* __restrict__ vc, const uint8_t* __restrict__ mask,
+    const u32x4* __restrict__ kc, const u32x4* __restrict__ vc, const uint8_t* __restrict__ mask,
     const int64_t* __restrict__ head_offsets, const int64_t* __restrict__ base,
-    uint4* __restrict__ ko, uint4* __restrict__ vo, int32_t* __restrict__ idx,
-    int64_t head_begin, int tiles_per_head, int n_c, int row_chunks) {
+    u32x4* __restrict__ ko, u32x4* __restrict__ vo, int32_t* __restrict__ idx,
+    int64_t head_begin, int tiles_per_head, int n_c) {
+  constexpr int U = 4;  // copies in flight per thread and array
   __shared__ uint32_t wtot[PER_T][4];
   __shared__ int32_t list[TILE];
   const int64_t tile = blockIdx.x;
@@ -87,21 +92,39 @@ __global__ __launch_bounds__(TPB) void cmp_scatter(
     run += wtot[u][0] + wtot[u][1] + wtot[u][2] + wtot[u][3];
   }
   __syncthreads();
-  const int count = run;
   const int64_t o0 = base[tile];
   // never write past this head's range, whatever the offsets say
   const int64_t lim = head_offsets[head_begin + hh + 1];
+  const int count = (int)max((int64_t)0, min((int64_t)run, lim - o0));
   const int64_t head_row0 = hh * (int64_t)n_c;  // k/v pointers start at head_begin
-  for (int k = t; k < count; k += TPB)
-    if (o0 + k < lim) idx[o0 + k] = list[k];
-  const int total = count * row_chunks;
-  for (int x = t; x < total; x += TPB) {
-    const int k = x / row_chunks, c = x - k * row_chunks;
-    const int64_t o = o0 + k;
-    if (o >= lim) continue;
-    const int64_t src = (head_row0 + list[k]) * row_chunks + c;
-    ko[o * row_chunks + c] = kc[src];
-    vo[o * row_chunks + c] = vc[src];
+  for (int k = t; k < count; k += TPB) idx[o0 + k] = list[k];
+  const int total = count * RC;
+  const u32x4* ksrc = kc + head_row0 * RC;
+  const u32x4* vsrc = vc + head_row0 * RC;
+  u32x4* kdst = ko + o0 * RC;
+  u32x4* vdst = vo + o0 * RC;
+  // U independent 16-byte copies per array per thread per round: all loads
+  // of a round are issued before its stores
+  for (int x0 = t; x0 < total; x0 += U * TPB) {
+    u32x4 kv[U], vv[U];
+#pragma unroll
+    for (int j = 0; j < U; ++j) {
+      const int x = x0 + j * TPB;
+      if (x < total) {
+        const int k = x / RC, c = x % RC;
+        const int64_t src = (int64_t)list[k] * RC + c;
+        kv[j] = ksrc[src];
+        vv[j] = vsrc[src];
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < U; ++j) {
+      const int x = x0 + j * TPB;
+      if (x < total) {
+        __builtin_nontemporal_store(kv[j], kdst + x);
+        __builtin_nontemporal_store(vv[j], vdst + x);
+      }
+    }
   }
 }
 
@@ -129,9 +152,18 @@ hipError_t compact_launch(const CompactPlan& p, int row_bytes, int64_t head_begi
              p.tiles_per_head, p.n_c);
   KVZ_LAUNCH("compact_scan", cmp_scan, (unsigned)((p.head_count + 255) / 256), 256, 0, st, cnt,
              head_offsets, base, head_begin, p.head_count, p.tiles_per_head);
-  KVZ_LAUNCH("compact_scatter", cmp_scatter, (unsigned)p.n_tiles, TPB, 0, st,
-             (const uint4*)kc, (const uint4*)vc, mask, head_offsets, base, (uint4*)ko,
-             (uint4*)vo, idx, head_begin, p.tiles_per_head, p.n_c, row_bytes / 16);
+#define KVZ_SCATTER(RC)                                                                   \
+  KVZ_LAUNCH("compact_scatter", cmp_scatter<RC>, (unsigned)p.n_tiles, TPB, 0, st,          \
+             (const u32x4*)kc, (const u32x4*)vc, mask, head_offsets, base, (u32x4*)ko,      \
+             (u32x4*)vo, idx, head_begin, p.tiles_per_head, p.n_c)
+  switch (row_bytes / 16) {
+    case 8: KVZ_SCATTER(8); break;
+    case 16: KVZ_SCATTER(16); break;
+    case 32: KVZ_SCATTER(32); break;
+    case 64: KVZ_SCATTER(64); break;
+    default: return hipErrorInvalidValue;
+  }
+#undef KVZ_SCATTER
   return hipGetLastError();
 }
 
