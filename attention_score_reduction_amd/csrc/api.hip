@@ -81,10 +81,13 @@ size_t kvz_score_chunk_workspace(kvz_dtype dt, int H, int G, int n_in, int d, in
   return score_plan(dt, H, G, n_in, d, n_c).total_bytes;
 }
 
-kvz_status kvz_score_chunk(kvz_dtype dt, int H, int G, int d, int n_c, int n_prompt, int n_in,
-                           const void* q, const void* k_ctx, const void* k_in, float scale,
-                           float* S, void* ws, size_t ws_bytes, void* stream) {
+kvz_status kvz_score_chunk_ex(kvz_dtype dt, kvz_aggregate agg, int H, int G, int d, int n_c,
+                              int n_prompt, int n_in, const void* q, const void* k_ctx,
+                              const void* k_in, float scale, float* S, void* ws, size_t ws_bytes,
+                              void* stream) {
   if (dt != KVZ_BF16 && dt != KVZ_F32) return KVZ_ERR_UNSUPPORTED;
+  if (agg != KVZ_AGG_MAX && agg != KVZ_AGG_SUM && agg != KVZ_AGG_RAW_MAX)
+    return KVZ_ERR_UNSUPPORTED;
   if (!head_dim_ok(d)) return KVZ_ERR_UNSUPPORTED;
   if (H < 1 || G < 1 || n_in < 1 || n_c < 1 || n_prompt < 0 || n_prompt > n_in)
     return KVZ_ERR_INVALID_ARG;
@@ -97,8 +100,37 @@ kvz_status kvz_score_chunk(kvz_dtype dt, int H, int G, int d, int n_c, int n_pro
   const ScorePlan p = score_plan(dt, H, G, n_in, d, n_c);
   if (ws_bytes < p.total_bytes) return KVZ_ERR_WORKSPACE;
   clear_error();
-  const hipError_t e = score_launch(dt, p, q, k_ctx, k_in, scale, S, ws,
+  const hipError_t e = score_launch(dt, agg, p, q, k_ctx, k_in, scale, S, ws,
                                     reinterpret_cast<hipStream_t>(stream));
+  return e == hipSuccess ? KVZ_OK : KVZ_ERR_HIP;
+}
+
+kvz_status kvz_score_chunk(kvz_dtype dt, int H, int G, int d, int n_c, int n_prompt, int n_in,
+                           const void* q, const void* k_ctx, const void* k_in, float scale,
+                           float* S, void* ws, size_t ws_bytes, void* stream) {
+  return kvz_score_chunk_ex(dt, KVZ_AGG_MAX, H, G, d, n_c, n_prompt, n_in, q, k_ctx, k_in, scale,
+                            S, ws, ws_bytes, stream);
+}
+
+kvz_status kvz_head_scores(const float* S, int64_t n_heads, int n_c, float* head_score,
+                           void* stream) {
+  if (n_heads < 1 || n_c < 1 || n_heads > (int64_t(1) << 31) - 1) return KVZ_ERR_INVALID_ARG;
+  if (!S || !head_score || !aligned16(S) || (reinterpret_cast<uintptr_t>(head_score) & 3u) != 0)
+    return KVZ_ERR_INVALID_ARG;
+  clear_error();
+  const hipError_t e =
+      head_scores_launch(S, n_heads, n_c, head_score, reinterpret_cast<hipStream_t>(stream));
+  return e == hipSuccess ? KVZ_OK : KVZ_ERR_HIP;
+}
+
+kvz_status kvz_token_scores(const float* S, int64_t n_heads, int n_c, float* token_score,
+                            void* stream) {
+  if (n_heads < 1 || n_c < 1) return KVZ_ERR_INVALID_ARG;
+  if (!S || !token_score || !aligned16(S) || (reinterpret_cast<uintptr_t>(token_score) & 3u) != 0)
+    return KVZ_ERR_INVALID_ARG;
+  clear_error();
+  const hipError_t e =
+      token_scores_launch(S, n_heads, n_c, token_score, reinterpret_cast<hipStream_t>(stream));
   return e == hipSuccess ? KVZ_OK : KVZ_ERR_HIP;
 }
 
@@ -194,7 +226,8 @@ kvz_status kvz_prof_read(const char* name, int64_t* launches, double* total_ms) 
                                  "select_empty",  "select_init",       "select_hist",
                                  "select_pick",   "select_tile_count", "select_scan",
                                  "select_mask",   "compact_count",     "compact_scan",
-                                 "compact_scatter"};
+                                 "compact_scatter", "head_scores",    "token_scores",
+                                 "decode_split",  "decode_combine"};
   for (const char* k : kNames) known |= strcmp(k, name) == 0;
   if (!known) return KVZ_ERR_INVALID_ARG;
   for (const ProfRec& r : p.recs) {

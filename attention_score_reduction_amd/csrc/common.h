@@ -61,8 +61,14 @@ struct ScorePlan {
   size_t part_bytes, lse_bytes, total_bytes;
 };
 ScorePlan score_plan(kvz_dtype dt, int H, int G, int n_in, int d, int n_c);
-hipError_t score_launch(kvz_dtype dt, const ScorePlan& p, const void* q, const void* kc,
-                        const void* kin, float scale, float* S, void* ws, hipStream_t st);
+hipError_t score_launch(kvz_dtype dt, kvz_aggregate agg, const ScorePlan& p, const void* q,
+                        const void* kc, const void* kin, float scale, float* S, void* ws,
+                        hipStream_t st);
+
+hipError_t head_scores_launch(const float* S, int64_t n_heads, int n_c, float* out,
+                              hipStream_t st);
+hipError_t token_scores_launch(const float* S, int64_t n_heads, int n_c, float* out,
+                               hipStream_t st);
 
 struct SelectPlan {
   int64_t N, n_heads;

@@ -355,11 +355,13 @@ __global__ __launch_bounds__(256) void score_combine(const float2* __restrict__ 
 // issues the MFMAs of row tile t+1 interleaved with the fma/max epilogue of
 // tile t, whose lse values were prefetched one iteration earlier.
 // ---------------------------------------------------------------------------
-template <int D>
+// MODE: 0 = max of probabilities (the method), 1 = sum of probabilities,
+// 2 = max of raw logits scale * q . k (no softmax; lse2 unused)
+template <int D, int MODE>
 __global__ __launch_bounds__(256) void score_pass2_bf16(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ kc,
     const float* __restrict__ lse2, float* __restrict__ S, int G, int n_c, int n_in, int R,
-    int R_pad, int n_kt, float cl2, int n_blocks) {
+    int R_pad, int n_kt, float cl2, float scale, int n_blocks) {
   constexpr int KS = Geo<D>::KS, CH = Geo<D>::CH, SWZ = Geo<D>::SWZ;
   constexpr int RT = 32;                     // query rows per tile
   constexpr int LOADS = RT * CH / 256;
@@ -428,9 +430,11 @@ __global__ __launch_bounds__(256) void score_pass2_bf16(
       c[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[ks], kr[1][ks], c[1], 0, 0, 0);
     }
   };
-  // two running maxima per column (alternating by element pair) keep the
-  // max chains short; each pair of elements costs two fma and one max3
-  float mx[2][2] = {{-INFINITY, -INFINITY}, {-INFINITY, -INFINITY}};
+  // two running accumulators per column (alternating by element pair) keep
+  // the dependency chains short; each pair of elements costs two fma and one
+  // max3 (MODE 0), two fma, two exp and two adds (MODE 1) or one max3 (MODE 2)
+  const float init = MODE == 1 ? 0.f : -INFINITY;
+  float mx[2][2] = {{init, init}, {init, init}};
   auto lse_of = [](const float4 (&L)[4], int v) {
     const float4 L4 = L[v >> 2];
     return (v & 3) == 0 ? L4.x : (v & 3) == 1 ? L4.y : (v & 3) == 2 ? L4.z : L4.w;
@@ -438,16 +442,23 @@ __global__ __launch_bounds__(256) void score_pass2_bf16(
   // elements e and e+1 (same column, e even)
   auto epi_pair = [&](const f32x16 (&c)[2], const float4 (&L)[4], int e) {
     const int col = e >> 4, v = e & 15;
-    const float t0 = fmaf(c[col][v], cl2, -lse_of(L, v));
-    const float t1 = fmaf(c[col][v + 1], cl2, -lse_of(L, v + 1));
     float& acc = mx[col][(v >> 1) & 1];
-    acc = fmaxf(acc, fmaxf(t0, t1));
+    if (MODE == 2) {
+      acc = fmaxf(acc, fmaxf(c[col][v], c[col][v + 1]));
+    } else {
+      const float t0 = fmaf(c[col][v], cl2, -lse_of(L, v));
+      const float t1 = fmaf(c[col][v + 1], cl2, -lse_of(L, v + 1));
+      if (MODE == 0)
+        acc = fmaxf(acc, fmaxf(t0, t1));
+      else
+        acc += fast_exp2(t0) + fast_exp2(t1);
+    }
   };
 
   // Tile t lives in LDS buffer t & 1; same schedule as pass 1 with the
   // fma/max epilogue of tile it spread over the MFMAs of tile it+1.
-  constexpr int NCH = 2 * KS;
-  constexpr int PER = 32 / NCH;
+  constexpr int NCH = 2 * KS;  // one chunk of epilogue work per MFMA: the 16
+                               // element pairs of a tile spread evenly
   f32x16 A[2], B[2];
   float4 LA[4], LB[4];
   load_tile(0);
@@ -471,7 +482,7 @@ __global__ __launch_bounds__(256) void score_pass2_bf16(
 #pragma unroll
     for (int c = 0; c < NCH; ++c) {
 #pragma unroll
-      for (int e = c * PER; e < (c + 1) * PER; e += 2) epi_pair(cur, Lc, e);
+      for (int pr = c * 16 / NCH; pr < (c + 1) * 16 / NCH; ++pr) epi_pair(cur, Lc, 2 * pr);
       __builtin_amdgcn_sched_barrier(0);
       const int ks = c >> 1, t = c & 1;
       nxt[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[ks], kr[t][ks], ks == 0 ? z : nxt[t],
@@ -496,18 +507,26 @@ __global__ __launch_bounds__(256) void score_pass2_bf16(
   } else {
     finish(A, LA);
   }
-  float mx0 = fmaxf(mx[0][0], mx[0][1]), mx1 = fmaxf(mx[1][0], mx[1][1]);
-
-  mx0 = fmaxf(mx0, __shfl_xor(mx0, 32));
-  mx1 = fmaxf(mx1, __shfl_xor(mx1, 32));
+  float r[2];
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    float v = MODE == 1 ? mx[t][0] + mx[t][1] : fmaxf(mx[t][0], mx[t][1]);
+    // lanes n and n+32 hold the same key column, different rows
+    const float o = __shfl_xor(v, 32);
+    r[t] = MODE == 1 ? v + o : fmaxf(v, o);
+  }
   if (half == 0) {
-    const float mxs[2] = {mx0, mx1};
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
       const int j = j0 + t * 32 + n;
       if (j < n_c) {
         float* sp = S + (size_t)h * n_c + j;
-        *sp = fmaxf(*sp, fminf(fast_exp2(mxs[t]), 1.0f));
+        if (MODE == 0)
+          *sp = fmaxf(*sp, fminf(fast_exp2(r[t]), 1.0f));
+        else if (MODE == 1)
+          *sp += r[t];
+        else
+          *sp = fmaxf(*sp, r[t] * scale);
       }
     }
   }
@@ -560,12 +579,13 @@ __global__ __launch_bounds__(64) void score_pass1_f32(const float* __restrict__ 
   if (r < R_pad) lse2[(size_t)h * R_pad + r] = (r < R) ? m + log2f(l) : INFINITY;
 }
 
-template <int D>
+template <int D, int MODE>
 __global__ __launch_bounds__(64) void score_pass2_f32(const float* __restrict__ q,
                                                       const float* __restrict__ kc,
                                                       const float* __restrict__ lse2,
                                                       float* __restrict__ S, int G, int n_c,
-                                                      int n_in, int R, int R_pad, float cl2) {
+                                                      int n_in, int R, int R_pad, float cl2,
+                                                      float scale) {
   __shared__ float ldk[D][64];
   __shared__ float ldq[32][D + 1];
   __shared__ float ldl[32];
@@ -574,7 +594,7 @@ __global__ __launch_bounds__(64) void score_pass2_f32(const float* __restrict__ 
   const int j = blockIdx.x * 64 + tid;
   for (int k = 0; k < D; ++k)
     ldk[k][tid] = (j < n_c) ? kc[((size_t)h * n_c + j) * D + k] : 0.f;
-  float mx = -INFINITY;
+  float mx = MODE == 1 ? 0.f : -INFINITY;
   for (int r0 = 0; r0 < R; r0 += 32) {
     __syncthreads();
     for (int e = tid; e < 32 * D; e += 64) {
@@ -591,47 +611,76 @@ __global__ __launch_bounds__(64) void score_pass2_f32(const float* __restrict__ 
     for (int rr = 0; rr < 32 && r0 + rr < R; ++rr) {
       float dot = 0.f;
       for (int k = 0; k < D; ++k) dot = fmaf(ldq[rr][k], ldk[k][tid], dot);
-      mx = fmaxf(mx, dot * cl2 - ldl[rr]);
+      if (MODE == 0) mx = fmaxf(mx, dot * cl2 - ldl[rr]);
+      else if (MODE == 1) mx += exp2f(dot * cl2 - ldl[rr]);
+      else mx = fmaxf(mx, dot);
     }
   }
   if (j < n_c) {
     float* sp = S + (size_t)h * n_c + j;
-    *sp = fmaxf(*sp, fminf(exp2f(mx), 1.0f));
+    if (MODE == 0) *sp = fmaxf(*sp, fminf(exp2f(mx), 1.0f));
+    else if (MODE == 1) *sp += mx;
+    else *sp = fmaxf(*sp, mx * scale);
   }
 }
 
-template <int D>
+template <int D, int MODE>
 hipError_t launch_bf16(const ScorePlan& p, const void* q, const void* kc, const void* kin,
-                       float cl2, float* S, void* ws, hipStream_t st) {
+                       float scale, float* S, void* ws, hipStream_t st) {
+  const float cl2 = scale * 1.4426950408889634f;
   float2* part = reinterpret_cast<float2*>(ws);
   float* lse2 = reinterpret_cast<float*>(reinterpret_cast<char*>(ws) + p.part_bytes);
   const int splits = p.n_split_ctx + 1;
-  const int nb1 = p.H * splits * p.n_rt;
-  KVZ_LAUNCH("score_pass1", score_pass1_bf16<D>, xcd_padded_grid(nb1), 256, 0, st,
-             (const uint16_t*)q, (const uint16_t*)kc, (const uint16_t*)kin, part, p.G, p.n_c,
-             p.n_in, p.R, p.R_pad, p.n_rt, p.n_split_ctx, p.tiles_per_split, cl2, nb1);
-  const int nc = p.H * p.R_pad;
-  KVZ_LAUNCH("score_combine", score_combine, (nc + 255) / 256, 256, 0, st, part, lse2, splits,
-             p.R, p.R_pad, p.H);
+  if (MODE != 2) {
+    const int nb1 = p.H * splits * p.n_rt;
+    KVZ_LAUNCH("score_pass1", score_pass1_bf16<D>, xcd_padded_grid(nb1), 256, 0, st,
+               (const uint16_t*)q, (const uint16_t*)kc, (const uint16_t*)kin, part, p.G, p.n_c,
+               p.n_in, p.R, p.R_pad, p.n_rt, p.n_split_ctx, p.tiles_per_split, cl2, nb1);
+    const int nc = p.H * p.R_pad;
+    KVZ_LAUNCH("score_combine", score_combine, (nc + 255) / 256, 256, 0, st, part, lse2, splits,
+               p.R, p.R_pad, p.H);
+  }
   const int n_kt = (p.n_c + P2_KEYS - 1) / P2_KEYS;
   const int nb2 = p.H * n_kt;
-  KVZ_LAUNCH("score_pass2", score_pass2_bf16<D>, xcd_padded_grid(nb2), 256, 0, st,
+  KVZ_LAUNCH("score_pass2", (score_pass2_bf16<D, MODE>), xcd_padded_grid(nb2), 256, 0, st,
              (const uint16_t*)q, (const uint16_t*)kc, lse2, S, p.G, p.n_c, p.n_in, p.R,
-             p.R_pad, n_kt, cl2, nb2);
+             p.R_pad, n_kt, cl2, scale, nb2);
   return hipGetLastError();
 }
 
-template <int D>
+template <int D, int MODE>
 hipError_t launch_f32(const ScorePlan& p, const void* q, const void* kc, const void* kin,
-                      float cl2, float* S, void* ws, hipStream_t st) {
+                      float scale, float* S, void* ws, hipStream_t st) {
+  const float cl2 = scale * 1.4426950408889634f;
   float* lse2 = reinterpret_cast<float*>(ws);
-  dim3 g1((p.R + 63) / 64, p.H);
-  KVZ_LAUNCH("score_pass1", score_pass1_f32<D>, g1, 64, 0, st, (const float*)q,
-             (const float*)kc, (const float*)kin, lse2, p.G, p.n_c, p.n_in, p.R, p.R_pad, cl2);
+  if (MODE != 2) {
+    dim3 g1((p.R + 63) / 64, p.H);
+    KVZ_LAUNCH("score_pass1", score_pass1_f32<D>, g1, 64, 0, st, (const float*)q,
+               (const float*)kc, (const float*)kin, lse2, p.G, p.n_c, p.n_in, p.R, p.R_pad, cl2);
+  }
   dim3 g2((p.n_c + 63) / 64, p.H);
-  KVZ_LAUNCH("score_pass2", score_pass2_f32<D>, g2, 64, 0, st, (const float*)q,
-             (const float*)kc, lse2, S, p.G, p.n_c, p.n_in, p.R, p.R_pad, cl2);
+  KVZ_LAUNCH("score_pass2", (score_pass2_f32<D, MODE>), g2, 64, 0, st, (const float*)q,
+             (const float*)kc, lse2, S, p.G, p.n_c, p.n_in, p.R, p.R_pad, cl2, scale);
   return hipGetLastError();
+}
+
+template <int MODE>
+hipError_t launch_mode(kvz_dtype dt, const ScorePlan& p, const void* q, const void* kc,
+                       const void* kin, float scale, float* S, void* ws, hipStream_t st) {
+  if (dt == KVZ_BF16) {
+    switch (p.d) {
+      case 64: return launch_bf16<64, MODE>(p, q, kc, kin, scale, S, ws, st);
+      case 128: return launch_bf16<128, MODE>(p, q, kc, kin, scale, S, ws, st);
+      case 256: return launch_bf16<256, MODE>(p, q, kc, kin, scale, S, ws, st);
+    }
+  } else {
+    switch (p.d) {
+      case 64: return launch_f32<64, MODE>(p, q, kc, kin, scale, S, ws, st);
+      case 128: return launch_f32<128, MODE>(p, q, kc, kin, scale, S, ws, st);
+      case 256: return launch_f32<256, MODE>(p, q, kc, kin, scale, S, ws, st);
+    }
+  }
+  return hipErrorInvalidValue;
 }
 
 }  // namespace
@@ -667,21 +716,13 @@ ScorePlan score_plan(kvz_dtype dt, int H, int G, int n_in, int d, int n_c) {
   return p;
 }
 
-hipError_t score_launch(kvz_dtype dt, const ScorePlan& p, const void* q, const void* kc,
-                        const void* kin, float scale, float* S, void* ws, hipStream_t st) {
-  const float cl2 = scale * 1.4426950408889634f;
-  if (dt == KVZ_BF16) {
-    switch (p.d) {
-      case 64: return launch_bf16<64>(p, q, kc, kin, cl2, S, ws, st);
-      case 128: return launch_bf16<128>(p, q, kc, kin, cl2, S, ws, st);
-      case 256: return launch_bf16<256>(p, q, kc, kin, cl2, S, ws, st);
-    }
-  } else {
-    switch (p.d) {
-      case 64: return launch_f32<64>(p, q, kc, kin, cl2, S, ws, st);
-      case 128: return launch_f32<128>(p, q, kc, kin, cl2, S, ws, st);
-      case 256: return launch_f32<256>(p, q, kc, kin, cl2, S, ws, st);
-    }
+hipError_t score_launch(kvz_dtype dt, kvz_aggregate agg, const ScorePlan& p, const void* q,
+                        const void* kc, const void* kin, float scale, float* S, void* ws,
+                        hipStream_t st) {
+  switch (agg) {
+    case KVZ_AGG_MAX: return launch_mode<0>(dt, p, q, kc, kin, scale, S, ws, st);
+    case KVZ_AGG_SUM: return launch_mode<1>(dt, p, q, kc, kin, scale, S, ws, st);
+    case KVZ_AGG_RAW_MAX: return launch_mode<2>(dt, p, q, kc, kin, scale, S, ws, st);
   }
   return hipErrorInvalidValue;
 }

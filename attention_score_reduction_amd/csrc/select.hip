@@ -3,9 +3,10 @@
 // KVzip sorts all KV pairs by importance and evicts the lowest (blog post,
 // section 4.1 step 5), with one threshold over all heads so that head
 // budgets come out non-uniform (atlas summary, "Measured effects").  Sorting
-// 33-65M floats is not needed: scores are >= 0, so their IEEE bit patterns
-// order like the values and the exact K-th largest score tau is found by a
-// radix select; then one tiled pass writes the mask: keep every score > tau
+// 33-65M floats is not needed: each float maps to a 32-bit key that orders
+// like the value (sign bit flipped for non-negative values, all bits flipped
+// for negative ones, -0 folded onto +0), the exact K-th largest key tau is
+// found by a radix select, then one tiled pass writes the mask: keep every score > tau
 // and the first (K - #greater) scores == tau in flat index order, which makes
 // exactly K.  Everything stays on the device (no host synchronisation) and
 // every atomic is an integer add, so the result is deterministic.
@@ -41,8 +42,15 @@ constexpr int TILE = 4096;        // scores per mask tile (within one head)
 constexpr int TPB = 256;          // threads per block
 constexpr int PER_T = TILE / TPB; // 16 scores per thread per tile
 
-// canonical key of a non-negative float (-0 and +0 compare equal)
-__device__ __forceinline__ uint32_t fkey(float f) { return __float_as_uint(f) & 0x7FFFFFFFu; }
+// order-preserving key of a non-NaN float (-0 and +0 compare equal)
+__device__ __forceinline__ uint32_t fkey(float f) {
+  uint32_t u = __float_as_uint(f);
+  if (u == 0x80000000u) u = 0u;
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ __forceinline__ float key_to_float(uint32_t k) {
+  return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
+}
 
 struct SelState {
   uint32_t b0, b1, tau, split_ties;  // digits found, tau bits, ties partially kept?
@@ -363,7 +371,7 @@ __global__ __launch_bounds__(SCAN_T) void sel_heads(const SelState* __restrict__
   }
   if (t == 0) {
     head_offsets[n_heads] = total;
-    *tau_out = __uint_as_float(st->tau);
+    *tau_out = key_to_float(st->tau);
   }
 }
 

@@ -15,12 +15,14 @@ LIB_PATH = os.path.join(HERE, "libkvz.so")
 
 KVZ_OK, KVZ_ERR_INVALID_ARG, KVZ_ERR_UNSUPPORTED, KVZ_ERR_WORKSPACE, KVZ_ERR_HIP = range(5)
 KVZ_BF16, KVZ_F32 = 0, 1
+KVZ_AGG_MAX, KVZ_AGG_SUM, KVZ_AGG_RAW_MAX = 0, 1, 2
+AGG = {"max": KVZ_AGG_MAX, "sum": KVZ_AGG_SUM, "raw": KVZ_AGG_RAW_MAX}
 
 # every symbol declared in include/kvz.h
 SYMBOLS = (
-    "kvz_status_string", "kvz_score_chunk_workspace", "kvz_score_chunk", "kvz_keep_count",
-    "kvz_select_workspace", "kvz_select_threshold", "kvz_compact_workspace", "kvz_compact",
-    "kvz_prof_enable", "kvz_prof_read",
+    "kvz_status_string", "kvz_score_chunk_workspace", "kvz_score_chunk", "kvz_score_chunk_ex",
+    "kvz_keep_count", "kvz_select_workspace", "kvz_select_threshold", "kvz_compact_workspace",
+    "kvz_compact", "kvz_head_scores", "kvz_token_scores", "kvz_prof_enable", "kvz_prof_read",
 )
 
 _lib = None
@@ -51,6 +53,13 @@ def lib():
     L.kvz_score_chunk.argtypes = [c_int, c_int, c_int, c_int, c_int, c_int, c_int, c_p, c_p, c_p,
                                   c_f, c_p, c_p, c_sz, c_p]
     L.kvz_score_chunk.restype = c_int
+    L.kvz_score_chunk_ex.argtypes = [c_int, c_int, c_int, c_int, c_int, c_int, c_int, c_int, c_p,
+                                     c_p, c_p, c_f, c_p, c_p, c_sz, c_p]
+    L.kvz_score_chunk_ex.restype = c_int
+    L.kvz_head_scores.argtypes = [c_p, c_i64, c_int, c_p, c_p]
+    L.kvz_head_scores.restype = c_int
+    L.kvz_token_scores.argtypes = [c_p, c_i64, c_int, c_p, c_p]
+    L.kvz_token_scores.restype = c_int
     L.kvz_keep_count.argtypes = [c_i64, c_d]
     L.kvz_keep_count.restype = c_i64
     L.kvz_select_workspace.argtypes = [c_i64, c_int]
@@ -127,6 +136,11 @@ def kvz_compact_workspace(head_count, n_c) -> int:
 def kvz_score_chunk(q, k_ctx, k_in, S, n_prompt, scale=None, ws=None, stream=None):
     """One reconstruction chunk of one layer.  q [H][G][n_in][d], k_ctx
     [H][n_c][d], k_in [H][n_in][d] (bf16 or fp32), S [H][n_c] fp32 in/out."""
+    return kvz_score_chunk_ex(q, k_ctx, k_in, S, n_prompt, "max", scale, ws, stream)
+
+
+def kvz_score_chunk_ex(q, k_ctx, k_in, S, n_prompt, agg="max", scale=None, ws=None, stream=None):
+    """kvz_score_chunk with aggregation agg in {"max", "sum", "raw"}."""
     import torch
     H, G, n_in, d = q.shape
     n_c = k_ctx.shape[1]
@@ -142,12 +156,34 @@ def kvz_score_chunk(q, k_ctx, k_in, S, n_prompt, scale=None, ws=None, stream=Non
     need = kvz_score_chunk_workspace(dt, H, G, n_in, d, n_c)
     if ws is None:
         ws = _ws(need, q.device)
-    st = lib().kvz_score_chunk(dt, H, G, d, n_c, int(n_prompt), n_in, _ptr(q, "q"),
-                               _ptr(k_ctx, "k_ctx"), _ptr(k_in, "k_in"), float(scale),
-                               _ptr(S, "S"), _ptr(ws, "ws"), ws.numel() * ws.element_size(),
-                               _stream(stream))
-    _check(st, "kvz_score_chunk")
+    st = lib().kvz_score_chunk_ex(dt, AGG[agg], H, G, d, n_c, int(n_prompt), n_in, _ptr(q, "q"),
+                                  _ptr(k_ctx, "k_ctx"), _ptr(k_in, "k_in"), float(scale),
+                                  _ptr(S, "S"), _ptr(ws, "ws"), ws.numel() * ws.element_size(),
+                                  _stream(stream))
+    _check(st, "kvz_score_chunk_ex")
     return S
+
+
+def kvz_head_scores(S, out=None, stream=None):
+    """[n_heads][n_c] fp32 -> [n_heads]: max over each head's tokens."""
+    import torch
+    n_heads, n_c = S.shape
+    if out is None:
+        out = torch.empty(n_heads, dtype=torch.float32, device=S.device)
+    _check(lib().kvz_head_scores(_ptr(S, "S"), n_heads, n_c, _ptr(out, "out"), _stream(stream)),
+           "kvz_head_scores")
+    return out
+
+
+def kvz_token_scores(S, out=None, stream=None):
+    """[n_heads][n_c] fp32 -> [n_c]: max over all heads per token."""
+    import torch
+    n_heads, n_c = S.shape
+    if out is None:
+        out = torch.empty(n_c, dtype=torch.float32, device=S.device)
+    _check(lib().kvz_token_scores(_ptr(S, "S"), n_heads, n_c, _ptr(out, "out"), _stream(stream)),
+           "kvz_token_scores")
+    return out
 
 
 def kvz_select_threshold(S, K, mask=None, head_offsets=None, tau=None, ws=None, stream=None):

@@ -63,6 +63,17 @@ typedef enum {
   KVZ_F32 = 1                  /* fp32 inputs, fp32 arithmetic              */
 } kvz_dtype;
 
+/* How a context key's per-row attention is aggregated into its score. */
+typedef enum {
+  KVZ_AGG_MAX = 0,     /* max over g, i of the softmax probability (the method,
+                          blog 4.3.2); S starts at 0                          */
+  KVZ_AGG_SUM = 1,     /* sum over g, i (and chunks) of the probability: the
+                          aggregation the rebuttal compares against (sum and
+                          mean rank keys identically); S starts at 0           */
+  KVZ_AGG_RAW_MAX = 2  /* max over g, i of the raw logit scale*q.k, no softmax
+                          (blog 5.5.5 ablation); S starts at -inf            */
+} kvz_aggregate;
+
 /* Human-readable name of a status code (static string, never NULL). */
 KVZ_API const char* kvz_status_string(kvz_status s);
 
@@ -98,6 +109,31 @@ KVZ_API kvz_status kvz_score_chunk(kvz_dtype dt, int H, int G, int d, int n_c, i
                            int n_in, const void* q, const void* k_ctx, const void* k_in,
                            float scale, float* S, void* ws, size_t ws_bytes, void* stream);
 
+/* kvz_score_chunk with a chosen aggregation (kvz_score_chunk == KVZ_AGG_MAX).
+ * KVZ_AGG_SUM: S[h][j] += sum over g, i of p[j] (running sum over chunks).
+ * KVZ_AGG_RAW_MAX: S[h][j] <- max(S[h][j], max over g, i of scale*q.k_j); no
+ * softmax is formed, so the in-chunk keys play no role.  Same arguments,
+ * workspace and errors as kvz_score_chunk; agg outside the enum ->
+ * KVZ_ERR_UNSUPPORTED. */
+KVZ_API kvz_status kvz_score_chunk_ex(kvz_dtype dt, kvz_aggregate agg, int H, int G, int d,
+                                      int n_c, int n_prompt, int n_in, const void* q,
+                                      const void* k_ctx, const void* k_in, float scale, float* S,
+                                      void* ws, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
+ * Head-level score (rebuttal, answer on head-level scores: the max of S along
+ * the sequence axis, used for context-independent head eviction):
+ *   head_score[h] = max over j of S[h][j]        (device fp32 [n_heads])
+ * Token-level score (blog 4.3.3: one score per token, max over layers and
+ * heads):
+ *   token_score[j] = max over h of S[h][j]       (device fp32 [n_c])
+ * S: device fp32 [n_heads][n_c], 16-byte aligned.  No workspace.
+ * ---------------------------------------------------------------------- */
+KVZ_API kvz_status kvz_head_scores(const float* S, int64_t n_heads, int n_c, float* head_score,
+                                   void* stream);
+KVZ_API kvz_status kvz_token_scores(const float* S, int64_t n_heads, int n_c, float* token_score,
+                                    void* stream);
+
 /* ------------------------------------------------------------------------
  * Keep count K = r * N rounded half up, clamped to [0, N] (host only).
  * ---------------------------------------------------------------------- */
@@ -108,8 +144,8 @@ KVZ_API int64_t kvz_keep_count(int64_t N, double r);
  * atlas, Approach and Measured effects).
  *
  *   S            device fp32 [n_heads][n_c], n_heads = L*H in flat (l, h)
- *                order; every score must be >= 0 and not NaN (scores from
- *                kvz_score_chunk are).
+ *                order; any values except NaN (raw-logit scores may be
+ *                negative); -0.0 ranks as +0.0.
  *   K            number of entries to keep, 0 <= K <= n_heads * n_c.
  *   mask         device uint8 [n_heads * n_c], out: 1 = kept.
  *   head_offsets device int64 [n_heads + 1], out: head_offsets[0] = 0 and

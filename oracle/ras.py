@@ -98,13 +98,20 @@ def chunk_probabilities(q_g, k_ctx_h, k_in_h, scale, rows=None):
     return e / e.sum(axis=1, keepdims=True)
 
 
-def score_chunk(q, k_ctx, k_in, scale, S, row_block=256):
+def score_chunk(q, k_ctx, k_in, scale, S, row_block=256, mode="max"):
     """Fold one reconstruction chunk into the running scores of one layer.
 
     q: [H][G][n_in][d], k_ctx: [H][n_c][d], k_in: [H][n_in][d], all float64.
-    S: [H][n_c] float64, updated in place:
-        S[h, j] = max(S[h, j], max over g and rows i of P_{h,g}[i, j]),
-    for context keys j only.  Returns S.
+    S: [H][n_c] float64, updated in place, for context keys j only:
+      mode "max" (the method, [blog] 4.3.2):
+          S[h, j] = max(S[h, j], max over g and rows i of P_{h,g}[i, j]);
+      mode "sum" (the aggregation the [rebuttal] answer on average
+          aggregation compares against; sum and mean rank keys alike):
+          S[h, j] += sum over g and rows i of P_{h,g}[i, j];
+      mode "raw" (the no-softmax ablation, [blog] 5.5.5 and [atlas] Measured
+          effects): S[h, j] = max(S[h, j], max over g, i of scale * q . k_j),
+          the unnormalised logit (start S at -inf).
+    Returns S.
     """
     H, G, n_in, _ = q.shape
     n_c = k_ctx.shape[1]
@@ -112,19 +119,44 @@ def score_chunk(q, k_ctx, k_in, scale, S, row_block=256):
         for g in range(G):
             for r0 in range(0, n_in, row_block):
                 rows = np.arange(r0, min(n_in, r0 + row_block))
+                if mode == "raw":
+                    x = (q[h, g][rows] @ k_ctx[h].T) * scale
+                    np.maximum(S[h], x.max(axis=0), out=S[h])
+                    continue
                 P = chunk_probabilities(q[h, g], k_ctx[h], k_in[h], scale, rows)
-                np.maximum(S[h], P[:, :n_c].max(axis=0), out=S[h])
+                if mode == "max":
+                    np.maximum(S[h], P[:, :n_c].max(axis=0), out=S[h])
+                elif mode == "sum":
+                    S[h] += P[:, :n_c].sum(axis=0)
+                else:
+                    raise ValueError(mode)
     return S
 
 
-def score_layer(chunks, k_ctx, scale):
+def score_layer(chunks, k_ctx, scale, mode="max"):
     """Scores of one layer from a list of chunks [(q, k_in), ...], S starting
-    at 0 (every probability is >= 0)."""
+    at 0 (max and sum of probabilities) or -inf (raw logits)."""
     H = k_ctx.shape[0]
-    S = np.zeros((H, k_ctx.shape[1]), np.float64)
+    S = np.full((H, k_ctx.shape[1]), -np.inf if mode == "raw" else 0.0)
     for q, k_in in chunks:
-        score_chunk(q, k_ctx, k_in, scale, S)
+        score_chunk(q, k_ctx, k_in, scale, S, mode=mode)
     return S
+
+
+# ---------------------------------------------------------------------------
+# head-level and token-level aggregates of S  ([rebuttal] answer on
+# head-level scores: max over the sequence axis of S[L][H][n_c]; [blog] 4.3.3:
+# one score per token as the max over layers and heads)
+# ---------------------------------------------------------------------------
+
+def head_scores(S2d):
+    """[n_heads][n_c] -> [n_heads]: max over the tokens of each head."""
+    return np.asarray(S2d).max(axis=1)
+
+
+def token_scores(S2d):
+    """[n_heads][n_c] -> [n_c]: max over all (layer, head) rows per token."""
+    return np.asarray(S2d).max(axis=0)
 
 
 # ---------------------------------------------------------------------------
@@ -155,6 +187,36 @@ def select(S_flat, n_heads: int, n_c: int, K: int):
     offsets = np.zeros(n_heads + 1, np.int64)
     offsets[1:] = np.cumsum(budget)
     return mask, offsets, tau
+
+
+# ---------------------------------------------------------------------------
+# decode attention over a packed per-head cache  ([abstract] and [atlas] Key
+# results: the compressed cache cuts FlashAttention decode latency about 2x;
+# [rebuttal] computational analysis: decode attention latency against the
+# kept ratio)
+# ---------------------------------------------------------------------------
+
+def decode_attention(q, k_out, v_out, head_offsets, scale):
+    """One decode token per query head over each KV head's kept rows.
+
+    q: [n_heads][G][d]; k_out, v_out: [K][d] packed rows, head h owning rows
+    head_offsets[h]..head_offsets[h+1]; all float64.  Returns
+    out[h, g] = softmax(scale * q[h, g] . K_h^T) @ V_h (zeros for an empty head).
+    """
+    n_heads, G, d = q.shape
+    out = np.zeros((n_heads, G, d))
+    for h in range(n_heads):
+        a, b = int(head_offsets[h]), int(head_offsets[h + 1])
+        if b == a:
+            continue
+        K = k_out[a:b]
+        V = v_out[a:b]
+        x = (q[h] @ K.T) * scale                       # [G][len]
+        x -= x.max(axis=1, keepdims=True)
+        p = np.exp(x)
+        p /= p.sum(axis=1, keepdims=True)
+        out[h] = p @ V
+    return out
 
 
 # ---------------------------------------------------------------------------

@@ -20,7 +20,7 @@ def _declared():
 def test_library_exports_every_declared_symbol():
     L = kvz.lib()
     names = _declared()
-    assert len(names) == 10
+    assert len(names) == len(set(kvz.SYMBOLS))
     assert sorted(kvz.SYMBOLS) == names
     for n in names:
         assert hasattr(L, n), n
@@ -82,6 +82,22 @@ def _score(**kw):
 ])
 def test_score_validation(kw, status):
     assert _score(**kw) == status
+
+
+def test_score_ex_rejects_unknown_aggregation():
+    L = kvz.lib()
+    r = L.kvz_score_chunk_ex(0, 7, 2, 4, 128, 100, 4, 20, FAKE, FAKE, FAKE, 0.1, FAKE, FAKE,
+                             1 << 30, None)
+    assert r == kvz.KVZ_ERR_UNSUPPORTED
+
+
+def test_head_token_validation():
+    L = kvz.lib()
+    assert L.kvz_head_scores(None, 4, 10, FAKE, None) == kvz.KVZ_ERR_INVALID_ARG
+    assert L.kvz_head_scores(FAKE, 0, 10, FAKE, None) == kvz.KVZ_ERR_INVALID_ARG
+    assert L.kvz_head_scores(MIS, 4, 10, FAKE, None) == kvz.KVZ_ERR_INVALID_ARG
+    assert L.kvz_token_scores(FAKE, 4, 0, FAKE, None) == kvz.KVZ_ERR_INVALID_ARG
+    assert L.kvz_token_scores(FAKE, 4, 10, None, None) == kvz.KVZ_ERR_INVALID_ARG
 
 
 def test_select_validation():

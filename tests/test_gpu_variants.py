@@ -1,0 +1,126 @@
+"""Parity of the aggregation variants (sum of probabilities, raw logits), the
+head-level and token-level score reductions, and selection over signed scores.
+
+Tolerances: sum of probabilities uses the method's allclose form
+(2e-3 + 1e-2 |ref|); raw logits (an fp32 dot product of bf16 inputs, no
+exponent) are held to 1e-4 + 1e-4 |ref|.
+"""
+import math
+
+import numpy as np
+import pytest
+
+from attention_score_reduction_amd import kvz
+from attention_score_reduction_amd.inputs import HostGen, Workload, bf16_bits
+from oracle import ras
+from tests.helpers import assert_scores_close, to_dev
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+CASES = [
+    # name, H, G, d, n_c, chunk, n_prompt, dtype
+    ("bf16_d128_g4", 2, 4, 128, 1000, 300, 16, "bf16"),
+    ("bf16_d64_g5", 1, 5, 64, 777, 250, 16, "bf16"),
+    ("bf16_d256_g2", 1, 2, 256, 900, 400, 16, "bf16"),
+    ("f32_d64_g2", 1, 2, 64, 512, 128, 8, "f32"),
+]
+
+
+def _scores(wl, agg, heads):
+    gen = HostGen(wl)
+    kc, _ = gen.context(0)
+    kc_d = to_dev(kc, wl.dtype)
+    init = -np.inf if agg == "raw" else 0.0
+    S = torch.full((wl.heads, wl.n_ctx), init, dtype=torch.float32, device="cuda")
+    ref = np.full((len(heads), wl.n_ctx), init)
+    scale = 1 / math.sqrt(wl.head_dim)
+    kc64 = ras.to_f64(gen.context(0, heads)[0], wl.dtype)
+    for k in range(len(wl.chunks())):
+        q, kin = gen.chunk_inputs(0, k)
+        kvz.kvz_score_chunk_ex(to_dev(q, wl.dtype), kc_d, to_dev(kin, wl.dtype), S, wl.n_prompt,
+                               agg, scale)
+        qs, ks = gen.chunk_inputs(0, k, heads)
+        ras.score_chunk(ras.to_f64(qs, wl.dtype), kc64, ras.to_f64(ks, wl.dtype), scale, ref,
+                        mode=agg)
+    torch.cuda.synchronize()
+    return S.cpu().numpy()[heads], ref
+
+
+@pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
+def test_sum_aggregation(case):
+    name, H, G, d, n_c, chunk, n_p, dt = case
+    wl = Workload(name, 21, 1, H, G, d, n_c, chunk, n_p, 0.3, dtype=dt, key_lognormal_sigma=0.5)
+    got, ref = _scores(wl, "sum", list(range(H)))
+    assert_scores_close(got, ref, what=f"sum {name}")
+
+
+@pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
+def test_raw_logit_aggregation(case):
+    name, H, G, d, n_c, chunk, n_p, dt = case
+    wl = Workload(name, 22, 1, H, G, d, n_c, chunk, n_p, 0.3, dtype=dt, key_lognormal_sigma=0.5)
+    got, ref = _scores(wl, "raw", list(range(H)))
+    assert_scores_close(got, ref, atol=1e-4, rtol=1e-4, what=f"raw {name}")
+
+
+def test_sum_and_raw_zero_query_closed_forms():
+    H, G, d, n_c, n_in = 2, 3, 128, 2000, 150
+    rng = np.random.default_rng(23)
+    kc = bf16_bits(rng.standard_normal((H, n_c, d)).astype(np.float32))
+    ki = bf16_bits(rng.standard_normal((H, n_in, d)).astype(np.float32))
+    q = bf16_bits(np.zeros((H, G, n_in, d), np.float32))
+    S = torch.zeros(H, n_c, dtype=torch.float32, device="cuda")
+    kvz.kvz_score_chunk_ex(to_dev(q, "bf16"), to_dev(kc, "bf16"), to_dev(ki, "bf16"), S, 10, "sum")
+    want = G * sum(1.0 / (n_c + i + 1) for i in range(n_in))
+    np.testing.assert_allclose(S.cpu().numpy(), want, rtol=1e-4)
+    R = torch.full((H, n_c), -np.inf, dtype=torch.float32, device="cuda")
+    kvz.kvz_score_chunk_ex(to_dev(q, "bf16"), to_dev(kc, "bf16"), to_dev(ki, "bf16"), R, 10, "raw")
+    assert np.all(R.cpu().numpy() == 0.0)
+
+
+def test_select_over_signed_raw_scores():
+    """Raw-logit scores are signed; selection must still be the exact top-K
+    of the oracle on the same fp32 values (including -0.0 and ties)."""
+    rng = np.random.default_rng(24)
+    S = (rng.standard_normal((12, 3001)) * 3).astype(np.float32)
+    S[2, :40] = -0.0
+    S[3, :40] = 0.0
+    S[5, 100:300] = S[5, 99]
+    for K in (1, 500, 18003, 36011, 36012):
+        m, o, t = kvz.kvz_select_threshold(torch.from_numpy(S).cuda(), K)
+        torch.cuda.synchronize()
+        rm, ro, rt = ras.select(S.reshape(-1), 12, 3001, K)
+        assert np.array_equal(m.cpu().numpy(), rm)
+        assert np.array_equal(o.cpu().numpy(), ro)
+        assert float(t.cpu()[0]) == np.float32(rt)
+
+
+@pytest.mark.parametrize("shape", [(1, 1), (3, 5), (256, 8192), (7, 100003)])
+def test_head_and_token_scores_exact(shape):
+    rng = np.random.default_rng(shape[0] * 7 + shape[1])
+    S = rng.random(shape).astype(np.float32)
+    Sd = torch.from_numpy(S).cuda()
+    hs = kvz.kvz_head_scores(Sd)
+    ts = kvz.kvz_token_scores(Sd)
+    torch.cuda.synchronize()
+    assert np.array_equal(hs.cpu().numpy(), ras.head_scores(S))
+    assert np.array_equal(ts.cpu().numpy(), ras.token_scores(S))
+
+
+def test_head_scores_of_scored_layer():
+    """Head-level scores of real scoring output: the head whose keys carry
+    the largest lognormal factor has the most peaked attention."""
+    wl = Workload("heads", 25, 1, 4, 2, 128, 1500, 500, 16, 0.3, key_lognormal_sigma=1.0, sink=True)
+    gen = HostGen(wl)
+    kc, _ = gen.context(0)
+    S = torch.zeros(wl.heads, wl.n_ctx, dtype=torch.float32, device="cuda")
+    for k in range(len(wl.chunks())):
+        q, kin = gen.chunk_inputs(0, k)
+        kvz.kvz_score_chunk(to_dev(q, "bf16"), to_dev(kc, "bf16"), to_dev(kin, "bf16"), S,
+                            wl.n_prompt)
+    hs = kvz.kvz_head_scores(S)
+    torch.cuda.synchronize()
+    assert np.array_equal(hs.cpu().numpy(), ras.head_scores(S.cpu().numpy()))
+    f = gen.key_factors(0)
+    assert int(np.argmax(hs.cpu().numpy())) == int(np.argmax(f))

@@ -279,3 +279,115 @@ def test_exact_fractions_for_three_token_case():
     S = ras.score_layer([(q, ki[None])], kc[None], 1.0)[0]
     want = [Fraction(1, 8), Fraction(2, 8), Fraction(3, 8)]
     np.testing.assert_allclose(S, [float(w) for w in want], rtol=1e-14)
+
+
+# ---------------------------------------------------------------------------
+# aggregation variants (sum / raw logits), head and token aggregates, decode
+# ---------------------------------------------------------------------------
+
+def test_sum_mode_zero_queries_closed_form():
+    """Q = 0: row i puts 1/(n_c + i + 1) on every context key, so the sum over
+    the G heads and n_in rows is G * sum_i 1/(n_c + i + 1) for every key."""
+    H, G, n_c, n_in, d = 2, 3, 40, 7, 8
+    q = np.zeros((H, G, n_in, d))
+    S = ras.score_layer([(q, _rand((H, n_in, d), 60))], _rand((H, n_c, d), 61), 0.3, mode="sum")
+    want = G * sum(1.0 / (n_c + i + 1) for i in range(n_in))
+    np.testing.assert_allclose(S, want, rtol=1e-14)
+
+
+def test_sum_mode_brute_force_and_mass():
+    H, G, n_c, n_in, d = 1, 2, 6, 4, 5
+    q = _rand((H, G, n_in, d), 62)
+    kc = _rand((H, n_c, d), 63)
+    ki = _rand((H, n_in, d), 64)
+    S = ras.score_layer([(q, ki)], kc, 0.4, mode="sum")[0]
+    want = [0.0] * n_c
+    chunk_mass = 0.0
+    for g in range(G):
+        for i in range(n_in):
+            keys = [kc[0, j] for j in range(n_c)] + [ki[0, t] for t in range(i + 1)]
+            lg = [0.4 * math.fsum(float(a) * float(b) for a, b in zip(q[0, g, i], k)) for k in keys]
+            z = math.fsum(math.exp(x) for x in lg)
+            for j in range(n_c):
+                want[j] += math.exp(lg[j]) / z
+            chunk_mass += math.fsum(math.exp(x) for x in lg[n_c:]) / z
+    np.testing.assert_allclose(S, want, rtol=1e-12)
+    # every row sums to one: context mass + chunk mass = G * n_in
+    assert math.isclose(S.sum() + chunk_mass, G * n_in, rel_tol=1e-12)
+
+
+def test_sum_and_mean_give_identical_priorities():
+    """The paperhub rebuttal's answer on average aggregation: sum and mean
+    rank keys identically (mean = sum / number of query rows)."""
+    H, G, n_c, d = 2, 2, 50, 8
+    chunks = [(_rand((H, G, n, d), 65 + n), _rand((H, n, d), 75 + n)) for n in (9, 6)]
+    kc = _rand((H, n_c, d), 66)
+    S_sum = ras.score_layer(chunks, kc, 0.35, mode="sum")
+    S_mean = S_sum / (G * (9 + 6))
+    K = 37
+    a = ras.select(S_sum.reshape(-1), H, n_c, K)[0]
+    b = ras.select(S_mean.reshape(-1), H, n_c, K)[0]
+    assert np.array_equal(a, b)
+
+
+def test_raw_mode_is_max_logit():
+    H, G, n_c, n_in, d = 2, 2, 30, 5, 8
+    q = _rand((H, G, n_in, d), 67)
+    kc = _rand((H, n_c, d), 68)
+    ki = _rand((H, n_in, d), 69)
+    S = ras.score_layer([(q, ki)], kc, 0.25, mode="raw")
+    for h in range(H):
+        for j in range(n_c):
+            want = max(0.25 * math.fsum(float(a) * float(b) for a, b in zip(q[h, g, i], kc[h, j]))
+                       for g in range(G) for i in range(n_in))
+            assert math.isclose(S[h, j], want, rel_tol=1e-12, abs_tol=1e-15)
+    S0 = ras.score_layer([(np.zeros_like(q), ki)], kc, 0.25, mode="raw")
+    assert np.all(S0 == 0.0)
+
+
+def test_raw_and_softmax_rank_differently():
+    """A key with a large logit in a row that also has a larger competitor
+    scores high raw but low after normalisation (what the ablation removes)."""
+    kc = np.array([[1.0, 0, 0], [0, 1.0, 0], [0, 0, 1.0]])   # A, B, C
+    ki = np.array([[0, 0, 0.0]])
+    q = np.array([[4.0, 6.0, 0.0]])                            # row sees A=4, B=6
+    raw = ras.score_layer([(q[None, None], ki[None])], kc[None], 1.0, mode="raw")[0]
+    mx = ras.score_layer([(q[None, None], ki[None])], kc[None], 1.0)[0]
+    q2 = np.array([[0.0, 0.0, 3.0]])                           # row sees C=3 alone
+    raw2 = ras.score_layer([(q2[None, None], ki[None])], kc[None], 1.0, mode="raw")[0]
+    mx2 = ras.score_layer([(q2[None, None], ki[None])], kc[None], 1.0)[0]
+    r = np.maximum(raw, raw2)
+    m = np.maximum(mx, mx2)
+    assert r[0] > r[2] and m[0] < m[2]
+
+
+def test_head_and_token_scores_brute_force():
+    rng = np.random.default_rng(70)
+    S = rng.random((6, 33))
+    hs = ras.head_scores(S)
+    ts = ras.token_scores(S)
+    assert hs.tolist() == [max(S[h].tolist()) for h in range(6)]
+    assert ts.tolist() == [max(S[:, j].tolist()) for j in range(33)]
+    assert np.all(S <= hs[:, None]) and np.all(S <= ts[None, :])
+
+
+def test_decode_attention_library_and_closed_forms():
+    torch = pytest.importorskip("torch")
+    rng = np.random.default_rng(71)
+    n_heads, G, d, L = 3, 4, 16, 9
+    q = rng.standard_normal((n_heads, G, d))
+    k = rng.standard_normal((n_heads * L, d))
+    v = rng.standard_normal((n_heads * L, d))
+    offs = np.arange(n_heads + 1) * L
+    out = ras.decode_attention(q, k, v, offs, 0.25)
+    for h in range(n_heads):
+        want = torch.nn.functional.scaled_dot_product_attention(
+            torch.from_numpy(q[h])[None], torch.from_numpy(k[h * L:(h + 1) * L])[None],
+            torch.from_numpy(v[h * L:(h + 1) * L])[None], scale=0.25)[0].numpy()
+        np.testing.assert_allclose(out[h], want, rtol=1e-12, atol=1e-14)
+    # one kept row: softmax of one logit is 1, the output is that V row;
+    # no kept row: zeros
+    offs2 = np.array([0, 1, 1, 3])
+    out2 = ras.decode_attention(q, k[:3], v[:3], offs2, 0.5)
+    np.testing.assert_allclose(out2[0], np.broadcast_to(v[0], (G, d)), rtol=0, atol=0)
+    assert np.all(out2[1] == 0.0)
