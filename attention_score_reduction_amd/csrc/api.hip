@@ -198,6 +198,34 @@ kvz_status kvz_compact(kvz_dtype dt, int d, int n_c, int64_t head_begin, int64_t
   return e == hipSuccess ? KVZ_OK : KVZ_ERR_HIP;
 }
 
+size_t kvz_decode_workspace(int64_t n_heads, int G, int d, int max_len) {
+  if (n_heads < 1 || G < 1 || G > 8 || !head_dim_ok(d) || max_len < 1) return 0;
+  return decode_plan(n_heads, G, d, max_len).total_bytes;
+}
+
+kvz_status kvz_decode_packed(kvz_dtype dt, int64_t n_heads, int G, int d, int max_len,
+                             const void* q, const void* k_rows, const void* v_rows,
+                             const int64_t* head_offsets, float scale, float* out, void* ws,
+                             size_t ws_bytes, void* stream) {
+  if (dt != KVZ_BF16 && dt != KVZ_F32) return KVZ_ERR_UNSUPPORTED;
+  if (!head_dim_ok(d) || G < 1 || G > 8) return KVZ_ERR_UNSUPPORTED;
+  if (n_heads < 1 || max_len < 1) return KVZ_ERR_INVALID_ARG;
+  if ((int64_t)n_heads * ((max_len + 1023) / 1024) >= (int64_t(1) << 31)) return KVZ_ERR_INVALID_ARG;
+  if (!q || !k_rows || !v_rows || !head_offsets || !out || !ws) return KVZ_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(k_rows) || !aligned16(v_rows) ||
+      (reinterpret_cast<uintptr_t>(head_offsets) & 7u) != 0 ||
+      (reinterpret_cast<uintptr_t>(out) & 3u) != 0 ||
+      (reinterpret_cast<uintptr_t>(ws) & 255u) != 0)
+    return KVZ_ERR_INVALID_ARG;
+  if (!(scale > 0.f) || !isfinite(scale)) return KVZ_ERR_INVALID_ARG;
+  const DecodePlan p = decode_plan(n_heads, G, d, max_len);
+  if (ws_bytes < p.total_bytes) return KVZ_ERR_WORKSPACE;
+  clear_error();
+  const hipError_t e = decode_launch(dt, p, q, k_rows, v_rows, head_offsets, scale, out, ws,
+                                     reinterpret_cast<hipStream_t>(stream));
+  return e == hipSuccess ? KVZ_OK : KVZ_ERR_HIP;
+}
+
 kvz_status kvz_prof_enable(int on, int max_launches) {
   Prof& p = prof();
   for (hipEvent_t e : p.pool) hipEventDestroy(e);

@@ -92,6 +92,16 @@ hipError_t compact_launch(const CompactPlan& p, int row_bytes, int64_t head_begi
                           const int64_t* head_offsets, void* ko, void* vo, int32_t* idx,
                           void* ws, hipStream_t st);
 
+struct DecodePlan {
+  int64_t n_heads;
+  int G, d, seg_rows, n_seg;
+  size_t total_bytes;
+};
+DecodePlan decode_plan(int64_t n_heads, int G, int d, int max_len);
+hipError_t decode_launch(kvz_dtype dt, const DecodePlan& p, const void* q, const void* k,
+                         const void* v, const int64_t* offs, float scale, float* out, void* ws,
+                         hipStream_t st);
+
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 }  // namespace kvz

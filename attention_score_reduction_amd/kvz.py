@@ -22,7 +22,8 @@ AGG = {"max": KVZ_AGG_MAX, "sum": KVZ_AGG_SUM, "raw": KVZ_AGG_RAW_MAX}
 SYMBOLS = (
     "kvz_status_string", "kvz_score_chunk_workspace", "kvz_score_chunk", "kvz_score_chunk_ex",
     "kvz_keep_count", "kvz_select_workspace", "kvz_select_threshold", "kvz_compact_workspace",
-    "kvz_compact", "kvz_head_scores", "kvz_token_scores", "kvz_prof_enable", "kvz_prof_read",
+    "kvz_compact", "kvz_head_scores", "kvz_token_scores", "kvz_decode_workspace",
+    "kvz_decode_packed", "kvz_prof_enable", "kvz_prof_read",
 )
 
 _lib = None
@@ -60,6 +61,11 @@ def lib():
     L.kvz_head_scores.restype = c_int
     L.kvz_token_scores.argtypes = [c_p, c_i64, c_int, c_p, c_p]
     L.kvz_token_scores.restype = c_int
+    L.kvz_decode_workspace.argtypes = [c_i64, c_int, c_int, c_int]
+    L.kvz_decode_workspace.restype = c_sz
+    L.kvz_decode_packed.argtypes = [c_int, c_i64, c_int, c_int, c_int, c_p, c_p, c_p, c_p, c_f,
+                                    c_p, c_p, c_sz, c_p]
+    L.kvz_decode_packed.restype = c_int
     L.kvz_keep_count.argtypes = [c_i64, c_d]
     L.kvz_keep_count.restype = c_i64
     L.kvz_select_workspace.argtypes = [c_i64, c_int]
@@ -225,6 +231,39 @@ def kvz_compact(k_ctx, v_ctx, mask, head_offsets, k_out, v_out, idx_out, head_be
                            ws.numel() * ws.element_size(), _stream(stream))
     _check(st, "kvz_compact")
     return k_out, v_out, idx_out
+
+
+def kvz_decode_workspace(n_heads, G, d, max_len) -> int:
+    return int(lib().kvz_decode_workspace(int(n_heads), int(G), int(d), int(max_len)))
+
+
+def kvz_decode_packed(q, k_rows, v_rows, head_offsets, max_len, scale=None, out=None, ws=None,
+                      stream=None):
+    """Decode attention: q [n_heads][G][d] over each head's rows of the packed
+    k_rows/v_rows [rows][d] (head h owns head_offsets[h]..head_offsets[h+1]).
+    Returns out [n_heads][G][d] fp32."""
+    import torch
+    n_heads, G, d = q.shape
+    if k_rows.dtype != q.dtype or v_rows.dtype != q.dtype:
+        raise TypeError("q, k_rows and v_rows must share a dtype")
+    if k_rows.shape[-1] != d or v_rows.shape != k_rows.shape:
+        raise ValueError("k_rows/v_rows must be [rows][d] with matching shapes")
+    if head_offsets.dtype != torch.int64 or head_offsets.numel() != n_heads + 1:
+        raise ValueError("head_offsets must be int64 [n_heads + 1]")
+    dt = _dtype_code(q)
+    if scale is None:
+        scale = d ** -0.5
+    if out is None:
+        out = torch.empty(n_heads, G, d, dtype=torch.float32, device=q.device)
+    if ws is None:
+        ws = _ws(kvz_decode_workspace(n_heads, G, d, max_len), q.device)
+    st = lib().kvz_decode_packed(dt, n_heads, G, d, int(max_len), _ptr(q, "q"),
+                                 _ptr(k_rows, "k_rows"), _ptr(v_rows, "v_rows"),
+                                 _ptr(head_offsets, "head_offsets"), float(scale),
+                                 _ptr(out, "out"), _ptr(ws, "ws"), ws.numel() * ws.element_size(),
+                                 _stream(stream))
+    _check(st, "kvz_decode_packed")
+    return out
 
 
 def kvz_prof_enable(on: bool, max_launches: int = 1 << 16):

@@ -106,6 +106,8 @@ def main():
     ap.add_argument("--layers", type=int, default=None, help="fewer layers (debug only)")
     ap.add_argument("--cpu-seconds", type=float, default=20.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-decode", action="store_true",
+                    help="skip the decode-attention comparison after the timed steps")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="after the timed steps, run a 2 GiB device-to-device copy (a plain copy "
                          "kernel of known size, to scale the HBM traffic counters)")
@@ -276,6 +278,38 @@ def main():
         "kernels": {k: {kk: round(vv, 3) if isinstance(vv, float) else vv for kk, vv in v.items()}
                     for k, v in kern.items()},
     }
+    # decode attention over the packed cache vs the full cache (one decode
+    # token per query head, all layers), outside the headline step
+    if not args.no_decode:
+        import torch as _t
+        gq = _t.Generator(device="cuda")
+        gq.manual_seed(wl.seed + 100)
+        q_dec = _t.randn(n_heads, G, d, generator=gq, device=dev).to(tdt)
+        offs_full = _t.arange(n_heads + 1, device=dev, dtype=_t.int64) * n_c
+        ws_dec = _t.empty(kvz.kvz_decode_workspace(n_heads, G, d, n_c), dtype=_t.uint8, device=dev)
+        out_dec = _t.empty(n_heads, G, d, dtype=_t.float32, device=dev)
+
+        def time_decode(k_rows, v_rows, offsets, reps=10):
+            for _ in range(2):
+                kvz.kvz_decode_packed(q_dec, k_rows, v_rows, offsets, n_c, out=out_dec, ws=ws_dec)
+            _t.cuda.synchronize()
+            t0 = time.perf_counter()
+            for _ in range(reps):
+                kvz.kvz_decode_packed(q_dec, k_rows, v_rows, offsets, n_c, out=out_dec, ws=ws_dec)
+            _t.cuda.synchronize()
+            return (time.perf_counter() - t0) / reps * 1e3
+
+        t_full = time_decode(kc_flat.view(-1, d), vc_flat.view(-1, d), offs_full)
+        t_kept = time_decode(k_out, v_out, offs)
+        elt = 2 if wl.dtype == "bf16" else 4
+        out["decode"] = {
+            "full_cache_ms": round(t_full, 4), "kept_cache_ms": round(t_kept, 4),
+            "speedup": round(t_full / t_kept, 3), "keep_ratio": wl.keep_ratio,
+            "full_GBs": round(2 * N * d * elt / (t_full * 1e-3) / 1e9, 1),
+            "kept_GBs": round(2 * K * d * elt / (t_kept * 1e-3) / 1e9, 1),
+            "what": f"one decode token for all {G * n_heads} query heads over all {n_heads} "
+                    "(layer, KV head) caches",
+        }
     if args.copy_calibration:
         nbytes = 2 << 30
         src_t = torch.ones(nbytes // 4, dtype=torch.float32, device=dev)

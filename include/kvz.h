@@ -188,6 +188,31 @@ KVZ_API kvz_status kvz_compact(kvz_dtype dt, int d, int n_c, int64_t head_begin,
                        int32_t* idx_out, void* ws, size_t ws_bytes, void* stream);
 
 /* ------------------------------------------------------------------------
+ * Decode attention over the packed per-head cache (abstract and atlas Key
+ * results: the compressed cache cuts FlashAttention decode latency about 2x;
+ * rebuttal, computational analysis: decode attention latency vs kept ratio).
+ * One decode token per query head:
+ *   out[h][g] = softmax(scale * q[h][g] . K_h^T) V_h      (zeros if K_h empty)
+ * with K_h, V_h = rows head_offsets[h] .. head_offsets[h+1]-1 of k_rows,
+ * v_rows.  Passing an uncompressed cache [n_heads][n_c][d] with
+ * head_offsets[h] = h * n_c gives full-cache decoding.
+ *   q             device [n_heads][G][d], element type dt, 16-byte aligned
+ *   k_rows,v_rows device [rows][d], element type dt, 16-byte aligned
+ *   head_offsets  device int64 [n_heads + 1], non-decreasing
+ *   max_len       host upper bound on every head's row count (rows of a head
+ *                 beyond it are not read)
+ *   out           device fp32 [n_heads][G][d]
+ * Limits: d in {64, 128, 256}, 1 <= G <= 8.  Workspace:
+ * kvz_decode_workspace() bytes (per-segment partial results).
+ * ---------------------------------------------------------------------- */
+KVZ_API size_t kvz_decode_workspace(int64_t n_heads, int G, int d, int max_len);
+
+KVZ_API kvz_status kvz_decode_packed(kvz_dtype dt, int64_t n_heads, int G, int d, int max_len,
+                                     const void* q, const void* k_rows, const void* v_rows,
+                                     const int64_t* head_offsets, float scale, float* out,
+                                     void* ws, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
  * Optional kernel timer (measurement only; not thread-safe).
  * While enabled, every kernel the library launches is bracketed by a pair of
  * HIP events on its stream.  kvz_prof_read() synchronises those events and

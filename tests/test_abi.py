@@ -100,6 +100,24 @@ def test_head_token_validation():
     assert L.kvz_token_scores(FAKE, 4, 10, None, None) == kvz.KVZ_ERR_INVALID_ARG
 
 
+def test_decode_validation():
+    L = kvz.lib()
+    f = lambda dt=0, nh=4, G=4, d=128, ml=100, q=FAKE, off=FAKE, out=FAKE, sc=0.1, ws=FAKE, wsb=1 << 30: \
+        L.kvz_decode_packed(dt, nh, G, d, ml, q, FAKE, FAKE, off, sc, out, ws, wsb, None)
+    assert f(G=9) == kvz.KVZ_ERR_UNSUPPORTED
+    assert f(G=0) == kvz.KVZ_ERR_UNSUPPORTED
+    assert f(d=96) == kvz.KVZ_ERR_UNSUPPORTED
+    assert f(nh=0) == kvz.KVZ_ERR_INVALID_ARG
+    assert f(ml=0) == kvz.KVZ_ERR_INVALID_ARG
+    assert f(q=None) == kvz.KVZ_ERR_INVALID_ARG
+    assert f(q=MIS) == kvz.KVZ_ERR_INVALID_ARG
+    assert f(off=P(4100)) == kvz.KVZ_ERR_INVALID_ARG
+    assert f(sc=-1.0) == kvz.KVZ_ERR_INVALID_ARG
+    assert f(wsb=8) == kvz.KVZ_ERR_WORKSPACE
+    assert kvz.kvz_decode_workspace(256, 4, 128, 131072) > 0
+    assert kvz.kvz_decode_workspace(256, 9, 128, 131072) == 0
+
+
 def test_select_validation():
     L = kvz.lib()
     f = lambda S=FAKE, nh=4, nc=10, K=5, m=FAKE, o=FAKE, t=FAKE, ws=FAKE, wsb=1 << 30: \

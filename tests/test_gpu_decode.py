@@ -1,0 +1,81 @@
+"""Decode attention over packed, variable-length per-head caches against the
+fp64 oracle (tolerance 1e-4 + 1e-3 |ref|: fp32 accumulation of bf16 inputs)."""
+import math
+
+import numpy as np
+import pytest
+
+from attention_score_reduction_amd import kvz
+from attention_score_reduction_amd.inputs import bf16_bits
+from oracle import ras
+from tests.helpers import assert_scores_close, to_dev
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+def _case(n_heads, G, d, lens, dtype, seed):
+    rng = np.random.default_rng(seed)
+    total = int(sum(lens))
+    q = rng.standard_normal((n_heads, G, d)).astype(np.float32)
+    k = (rng.standard_normal((total, d)) * 1.5).astype(np.float32)
+    v = rng.standard_normal((total, d)).astype(np.float32)
+    if dtype == "bf16":
+        q, k, v = bf16_bits(q), bf16_bits(k), bf16_bits(v)
+    offs = np.zeros(n_heads + 1, np.int64)
+    offs[1:] = np.cumsum(lens)
+    scale = 1 / math.sqrt(d)
+    out = kvz.kvz_decode_packed(to_dev(q, dtype), to_dev(k, dtype), to_dev(v, dtype),
+                                torch.from_numpy(offs).cuda(), max(max(lens), 1), scale)
+    torch.cuda.synchronize()
+    ref = ras.decode_attention(ras.to_f64(q, dtype), ras.to_f64(k, dtype), ras.to_f64(v, dtype),
+                               offs, scale)
+    return out.cpu().numpy(), ref
+
+
+@pytest.mark.parametrize("d", [64, 128, 256])
+@pytest.mark.parametrize("G", [1, 2, 4, 5, 8])
+def test_decode_variable_lengths(d, G):
+    lens = [0, 1, 3, 17, 64, 1023, 1024, 1025, 5000]
+    got, ref = _case(len(lens), G, d, lens, "bf16", d * 10 + G)
+    assert_scores_close(got, ref, atol=1e-4, rtol=1e-3, what=f"decode d={d} G={G}")
+
+
+def test_decode_fp32_and_dense_baseline():
+    got, ref = _case(3, 4, 64, [700, 0, 2500], "f32", 5)
+    assert_scores_close(got, ref, atol=1e-4, rtol=1e-3, what="decode fp32")
+    # uniform offsets over an uncompressed cache: the full-cache baseline
+    got, ref = _case(8, 4, 128, [4096] * 8, "bf16", 6)
+    assert_scores_close(got, ref, atol=1e-4, rtol=1e-3, what="decode dense")
+
+
+def test_decode_on_compacted_cache_matches_kept_rows():
+    """Select + compact a cache, decode on the packed result; the oracle
+    decodes over each head's kept rows taken straight from the source."""
+    rng = np.random.default_rng(7)
+    n_heads, n_c, d, G = 6, 3000, 128, 4
+    kc = bf16_bits(rng.standard_normal((n_heads, n_c, d)).astype(np.float32))
+    vc = bf16_bits(rng.standard_normal((n_heads, n_c, d)).astype(np.float32))
+    S = rng.random((n_heads, n_c)).astype(np.float32)
+    S[2] *= 0.2
+    K = kvz.kvz_keep_count(S.size, 0.3)
+    mask, offs, _ = kvz.kvz_select_threshold(torch.from_numpy(S).cuda(), K)
+    ko = torch.empty(K, d, dtype=torch.bfloat16, device="cuda")
+    vo = torch.empty_like(ko)
+    idx = torch.empty(K, dtype=torch.int32, device="cuda")
+    kvz.kvz_compact(to_dev(kc, "bf16"), to_dev(vc, "bf16"), mask, offs, ko, vo, idx)
+    q = bf16_bits(rng.standard_normal((n_heads, G, d)).astype(np.float32))
+    out = kvz.kvz_decode_packed(to_dev(q, "bf16"), ko, vo, offs, n_c)
+    torch.cuda.synchronize()
+    m = mask.cpu().numpy().reshape(n_heads, n_c).astype(bool)
+    o = offs.cpu().numpy()
+    ref = np.zeros((n_heads, G, d))
+    for h in range(n_heads):
+        js = np.nonzero(m[h])[0]
+        assert len(js) == o[h + 1] - o[h]
+        kk = ras.bf16_to_f64(kc[h, js])
+        vv = ras.bf16_to_f64(vc[h, js])
+        ref[h] = ras.decode_attention(ras.bf16_to_f64(q[h:h + 1]), kk, vv,
+                                      np.array([0, len(js)]), 1 / math.sqrt(d))[0]
+    assert_scores_close(out.cpu().numpy(), ref, atol=1e-4, rtol=1e-3, what="decode packed")
