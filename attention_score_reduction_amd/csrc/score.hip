@@ -34,7 +34,6 @@ namespace {
 
 constexpr int KT = 32;          // keys per pass-1 tile
 constexpr int P1_ROWS = 256;    // query rows per pass-1 workgroup (4 waves x 64)
-constexpr int P2_KEYS = 256;    // context keys per pass-2 workgroup (4 waves x 64)
 constexpr float kNegBig = -1e30f;
 
 #ifndef KVZ_P1_TARGET_WGS
@@ -52,9 +51,6 @@ template <int CH, int SWZ>
 __device__ __forceinline__ int swz(int row, int ch) {
   return row * CH + (ch ^ (row & SWZ));
 }
-
-// scheduling-group masks of __builtin_amdgcn_sched_group_barrier
-constexpr int SG_VALU = 0x002, SG_MFMA = 0x008, SG_VMEM_READ = 0x020, SG_DS_READ = 0x100;
 
 // Exact online max/sum of 16 logits (raw dot products) into (m, l), log2
 // domain: raise m to the tile max, rescale l, add the tile's terms.
@@ -348,21 +344,30 @@ __global__ __launch_bounds__(256) void score_combine(const float2* __restrict__ 
 
 // ---------------------------------------------------------------------------
 // pass 2, bf16: column max over all query rows, running max into S
-// grid: H x key-tiles of 256 (XCD-remapped: head-major)
+// grid: H x key blocks (XCD-remapped: head-major)
 //
-// Same pipeline as pass 1 with the roles swapped: each wave keeps 64 context
-// keys in registers and sweeps 32-row query tiles staged in LDS; iteration t
-// issues the MFMAs of row tile t+1 interleaved with the fma/max epilogue of
-// tile t, whose lse values were prefetched one iteration earlier.
-// ---------------------------------------------------------------------------
+// Each wave keeps NT 32-key tiles of K in registers (128 keys for d <= 128)
+// and sweeps 32-row query tiles staged in LDS (double buffer, one barrier per
+// tile); every A operand read from LDS feeds NT MFMAs.  The epilogue of a key
+// tile (fma with the row lse and a running max, or the sum / raw variants)
+// overlaps the MFMAs of the following key tiles of the same query tile.
+// Padding rows (r >= R) re-read row R-1 and carry lse = +inf.
 // MODE: 0 = max of probabilities (the method), 1 = sum of probabilities,
 // 2 = max of raw logits scale * q . k (no softmax; lse2 unused)
+// ---------------------------------------------------------------------------
+template <int D>
+struct P2Shape {
+  static constexpr int NT = D <= 128 ? 4 : 2;    // key tiles per wave
+  static constexpr int KEYS = 4 * 32 * NT;       // keys per workgroup
+};
+
 template <int D, int MODE>
 __global__ __launch_bounds__(256) void score_pass2_bf16(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ kc,
     const float* __restrict__ lse2, float* __restrict__ S, int G, int n_c, int n_in, int R,
     int R_pad, int n_kt, float cl2, float scale, int n_blocks) {
   constexpr int KS = Geo<D>::KS, CH = Geo<D>::CH, SWZ = Geo<D>::SWZ;
+  constexpr int NT = P2Shape<D>::NT;
   constexpr int RT = 32;                     // query rows per tile
   constexpr int LOADS = RT * CH / 256;
   __shared__ uint4 ldq[2][RT * CH];
@@ -373,33 +378,26 @@ __global__ __launch_bounds__(256) void score_pass2_bf16(
   const int h = lb / n_kt;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int n = lane & 31, half = lane >> 5;
-  const int j0 = kt * P2_KEYS + wave * 64;
+  const int j0 = kt * P2Shape<D>::KEYS + wave * (32 * NT);
 
-  // stationary key operand (B of Q*K^T): this lane's key column n
-  bf16x8 kr[2][KS];
+  // stationary key operand (B of Q*K^T): this lane's key column n of each
+  // tile; keys past n_c re-read key n_c - 1 and are never written back
+  bf16x8 kr[NT][KS];
 #pragma unroll
-  for (int t = 0; t < 2; ++t) {
-    const int j = j0 + t * 32 + n;
-    if (j < n_c) {
-      const uint16_t* p = kc + ((size_t)h * n_c + j) * D + half * 8;
+  for (int t = 0; t < NT; ++t) {
+    const int j = min(j0 + t * 32 + n, n_c - 1);
+    const uint16_t* p = kc + ((size_t)h * n_c + j) * D + half * 8;
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) kr[t][ks] = as_bf16x8(ld16(p + ks * 16));
-    } else {
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) kr[t][ks] = as_bf16x8(make_uint4(0, 0, 0, 0));
-    }
+    for (int ks = 0; ks < KS; ++ks) kr[t][ks] = as_bf16x8(ld16(p + ks * 16));
   }
 
   const float* lseh = lse2 + (size_t)h * R_pad;
   const uint16_t* qh = q + (size_t)h * R * D;  // rows of head h, g-major: g * n_in + i
   const int n_tiles = R_pad / RT;
-  const int last = n_tiles - 1;
   uint4 reg[LOADS];
   auto load_tile = [&](int t) {
 #pragma unroll
     for (int u = 0; u < LOADS; ++u) {
-      // padding rows (r >= R) re-read row R-1; their lse is +inf, so they
-      // never win the max and need no zero fill (and no branch)
       const int c = tid + 256 * u, row = c / CH, ch = c % CH, rr = min(t * RT + row, R - 1);
       reg[u] = ld16(qh + (size_t)rr * D + ch * 8);
     }
@@ -411,123 +409,82 @@ __global__ __launch_bounds__(256) void score_pass2_bf16(
       ldq[buf][swz<CH, SWZ>(row, ch)] = reg[u];
     }
   };
-  // lse of the 16 rows this lane holds in the MFMA output of tile t
-  auto load_lse = [&](int t, float4 (&L)[4]) {
-#pragma unroll
-    for (int vg = 0; vg < 4; ++vg)
-      L[vg] = *reinterpret_cast<const float4*>(lseh + t * RT + 8 * vg + 4 * half);
-  };
-  auto mfma_tile = [&](int buf, f32x16 (&c)[2]) {
-    bf16x8 a[KS];
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) a[ks] = as_bf16x8(ldq[buf][swz<CH, SWZ>(n, ks * 2 + half)]);
-    const f32x16 z = {};
-    c[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[0], kr[0][0], z, 0, 0, 0);
-    c[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[0], kr[1][0], z, 0, 0, 0);
-#pragma unroll
-    for (int ks = 1; ks < KS; ++ks) {
-      c[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[ks], kr[0][ks], c[0], 0, 0, 0);
-      c[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[ks], kr[1][ks], c[1], 0, 0, 0);
-    }
-  };
-  // two running accumulators per column (alternating by element pair) keep
-  // the dependency chains short; each pair of elements costs two fma and one
-  // max3 (MODE 0), two fma, two exp and two adds (MODE 1) or one max3 (MODE 2)
-  const float init = MODE == 1 ? 0.f : -INFINITY;
-  float mx[2][2] = {{init, init}, {init, init}};
-  auto lse_of = [](const float4 (&L)[4], int v) {
-    const float4 L4 = L[v >> 2];
-    return (v & 3) == 0 ? L4.x : (v & 3) == 1 ? L4.y : (v & 3) == 2 ? L4.z : L4.w;
-  };
-  // elements e and e+1 (same column, e even)
-  auto epi_pair = [&](const f32x16 (&c)[2], const float4 (&L)[4], int e) {
-    const int col = e >> 4, v = e & 15;
-    float& acc = mx[col][(v >> 1) & 1];
-    if (MODE == 2) {
-      acc = fmaxf(acc, fmaxf(c[col][v], c[col][v + 1]));
-    } else {
-      const float t0 = fmaf(c[col][v], cl2, -lse_of(L, v));
-      const float t1 = fmaf(c[col][v + 1], cl2, -lse_of(L, v + 1));
-      if (MODE == 0)
-        acc = fmaxf(acc, fmaxf(t0, t1));
-      else
-        acc += fast_exp2(t0) + fast_exp2(t1);
-    }
-  };
 
-  // Tile t lives in LDS buffer t & 1; same schedule as pass 1 with the
-  // fma/max epilogue of tile it spread over the MFMAs of tile it+1.
-  constexpr int NCH = 2 * KS;  // one chunk of epilogue work per MFMA: the 16
-                               // element pairs of a tile spread evenly
-  f32x16 A[2], B[2];
-  float4 LA[4], LB[4];
+  const float init = MODE == 1 ? 0.f : -INFINITY;
+  float acc[NT];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) acc[t] = init;
+
   load_tile(0);
   store_tile(0);
-  load_lse(0, LA);
   __syncthreads();
-  load_tile(min(1, last));
-  mfma_tile(0, A);
-  store_tile(1);
-  __syncthreads();
-  auto body = [&](int it, f32x16 (&cur)[2], f32x16 (&nxt)[2], const float4 (&Lc)[4],
-                  float4 (&Ln)[4]) {
-    load_tile(min(it + 2, last));
-    load_lse(it + 1, Ln);
-    const int buf = (it + 1) & 1;
+  for (int it = 0; it < n_tiles; ++it) {
+    const int buf = it & 1;
+    if (it + 1 < n_tiles) load_tile(it + 1);
+    // lse of the 16 rows this lane holds in the MFMA output
+    float4 L[4];
+    if (MODE != 2) {
+#pragma unroll
+      for (int vg = 0; vg < 4; ++vg)
+        L[vg] = *reinterpret_cast<const float4*>(lseh + it * RT + 8 * vg + 4 * half);
+    }
     bf16x8 a[KS];
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) a[ks] = as_bf16x8(ldq[buf][swz<CH, SWZ>(n, ks * 2 + half)]);
-    __builtin_amdgcn_sched_barrier(0);
+    f32x16 c[NT];
     const f32x16 z = {};
 #pragma unroll
-    for (int c = 0; c < NCH; ++c) {
+    for (int t = 0; t < NT; ++t) {
 #pragma unroll
-      for (int pr = c * 16 / NCH; pr < (c + 1) * 16 / NCH; ++pr) epi_pair(cur, Lc, 2 * pr);
-      __builtin_amdgcn_sched_barrier(0);
-      const int ks = c >> 1, t = c & 1;
-      nxt[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[ks], kr[t][ks], ks == 0 ? z : nxt[t],
-                                                       0, 0, 0);
-      __builtin_amdgcn_sched_barrier(0);
+      for (int ks = 0; ks < KS; ++ks)
+        c[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[ks], kr[t][ks], ks == 0 ? z : c[t], 0, 0,
+                                                       0);
     }
-    store_tile(it & 1);
-    __syncthreads();
-  };
-  auto finish = [&](const f32x16 (&cur)[2], const float4 (&Lc)[4]) {
 #pragma unroll
-    for (int e = 0; e < 32; e += 2) epi_pair(cur, Lc, e);
-  };
-  int it = 0;
-  for (; it + 2 < n_tiles; it += 2) {
-    body(it, A, B, LA, LB);
-    body(it + 1, B, A, LB, LA);
-  }
-  if (it + 1 < n_tiles) {
-    body(it, A, B, LA, LB);
-    finish(B, LB);
-  } else {
-    finish(A, LA);
-  }
-  float r[2];
+    for (int t = 0; t < NT; ++t) {
 #pragma unroll
-  for (int t = 0; t < 2; ++t) {
-    float v = MODE == 1 ? mx[t][0] + mx[t][1] : fmaxf(mx[t][0], mx[t][1]);
-    // lanes n and n+32 hold the same key column, different rows
-    const float o = __shfl_xor(v, 32);
-    r[t] = MODE == 1 ? v + o : fmaxf(v, o);
-  }
-  if (half == 0) {
+      for (int vg = 0; vg < 4; ++vg) {
+        float lv[4] = {0.f, 0.f, 0.f, 0.f};
+        if (MODE != 2) {
+          lv[0] = L[vg].x;
+          lv[1] = L[vg].y;
+          lv[2] = L[vg].z;
+          lv[3] = L[vg].w;
+        }
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      const int j = j0 + t * 32 + n;
-      if (j < n_c) {
-        float* sp = S + (size_t)h * n_c + j;
-        if (MODE == 0)
-          *sp = fmaxf(*sp, fminf(fast_exp2(r[t]), 1.0f));
-        else if (MODE == 1)
-          *sp += r[t];
-        else
-          *sp = fmaxf(*sp, r[t] * scale);
+        for (int e = 0; e < 4; e += 2) {
+          const float x0 = c[t][vg * 4 + e], x1 = c[t][vg * 4 + e + 1];
+          if (MODE == 2) {
+            acc[t] = fmaxf(acc[t], fmaxf(x0, x1));
+          } else {
+            const float t0 = fmaf(x0, cl2, -lv[e]);
+            const float t1 = fmaf(x1, cl2, -lv[e + 1]);
+            if (MODE == 0)
+              acc[t] = fmaxf(acc[t], fmaxf(t0, t1));
+            else
+              acc[t] += fast_exp2(t0) + fast_exp2(t1);
+          }
+        }
       }
+    }
+    if (it + 1 < n_tiles) store_tile(buf ^ 1);
+    __syncthreads();
+  }
+
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    // lanes n and n+32 hold the same key column, different rows
+    const float o = __shfl_xor(acc[t], 32);
+    const float r = MODE == 1 ? acc[t] + o : fmaxf(acc[t], o);
+    const int j = j0 + t * 32 + n;
+    if (half == 0 && j < n_c) {
+      float* sp = S + (size_t)h * n_c + j;
+      if (MODE == 0)
+        *sp = fmaxf(*sp, fminf(fast_exp2(r), 1.0f));
+      else if (MODE == 1)
+        *sp += r;
+      else
+        *sp = fmaxf(*sp, r * scale);
     }
   }
 }
@@ -640,7 +597,7 @@ hipError_t launch_bf16(const ScorePlan& p, const void* q, const void* kc, const 
     KVZ_LAUNCH("score_combine", score_combine, (nc + 255) / 256, 256, 0, st, part, lse2, splits,
                p.R, p.R_pad, p.H);
   }
-  const int n_kt = (p.n_c + P2_KEYS - 1) / P2_KEYS;
+  const int n_kt = (p.n_c + P2Shape<D>::KEYS - 1) / P2Shape<D>::KEYS;
   const int nb2 = p.H * n_kt;
   KVZ_LAUNCH("score_pass2", (score_pass2_bf16<D, MODE>), xcd_padded_grid(nb2), 256, 0, st,
              (const uint16_t*)q, (const uint16_t*)kc, lse2, S, p.G, p.n_c, p.n_in, p.R,
