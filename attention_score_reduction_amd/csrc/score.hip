@@ -415,12 +415,35 @@ __global__ __launch_bounds__(256) void score_pass2_bf16(
 #pragma unroll
   for (int t = 0; t < NT; ++t) acc[t] = init;
 
+  // epilogue of one key tile: elements 2p, 2p+1 for p in [p0, p1)
+  auto epilogue = [&](const f32x16& c, const float4 (&L)[4], int t, int p0, int p1) {
+#pragma unroll
+    for (int pr = p0; pr < p1; ++pr) {
+      const int v = 2 * pr;
+      const float x0 = c[v], x1 = c[v + 1];
+      if (MODE == 2) {
+        acc[t] = fmaxf(acc[t], fmaxf(x0, x1));
+      } else {
+        const float4 L4 = L[v >> 2];
+        const float l0 = (v & 3) == 0 ? L4.x : L4.z, l1 = (v & 3) == 0 ? L4.y : L4.w;
+        const float t0 = fmaf(x0, cl2, -l0);
+        const float t1 = fmaf(x1, cl2, -l1);
+        if (MODE == 0)
+          acc[t] = fmaxf(acc[t], fmaxf(t0, t1));
+        else
+          acc[t] += fast_exp2(t0) + fast_exp2(t1);
+      }
+    }
+  };
+
   load_tile(0);
   store_tile(0);
   __syncthreads();
   for (int it = 0; it < n_tiles; ++it) {
     const int buf = it & 1;
-    if (it + 1 < n_tiles) load_tile(it + 1);
+    // the last iteration re-loads and re-stores its own tile into the idle
+    // buffer (never read again): no branch in the loop body
+    load_tile(min(it + 1, n_tiles - 1));
     // lse of the 16 rows this lane holds in the MFMA output
     float4 L[4];
     if (MODE != 2) {
@@ -433,41 +456,20 @@ __global__ __launch_bounds__(256) void score_pass2_bf16(
     for (int ks = 0; ks < KS; ++ks) a[ks] = as_bf16x8(ldq[buf][swz<CH, SWZ>(n, ks * 2 + half)]);
     f32x16 c[NT];
     const f32x16 z = {};
+    __builtin_amdgcn_sched_barrier(0);
+    // MFMAs of key tile t, each followed by a share of key tile t-1's epilogue
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks)
+      for (int ks = 0; ks < KS; ++ks) {
         c[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[ks], kr[t][ks], ks == 0 ? z : c[t], 0, 0,
                                                        0);
-    }
-#pragma unroll
-    for (int t = 0; t < NT; ++t) {
-#pragma unroll
-      for (int vg = 0; vg < 4; ++vg) {
-        float lv[4] = {0.f, 0.f, 0.f, 0.f};
-        if (MODE != 2) {
-          lv[0] = L[vg].x;
-          lv[1] = L[vg].y;
-          lv[2] = L[vg].z;
-          lv[3] = L[vg].w;
-        }
-#pragma unroll
-        for (int e = 0; e < 4; e += 2) {
-          const float x0 = c[t][vg * 4 + e], x1 = c[t][vg * 4 + e + 1];
-          if (MODE == 2) {
-            acc[t] = fmaxf(acc[t], fmaxf(x0, x1));
-          } else {
-            const float t0 = fmaf(x0, cl2, -lv[e]);
-            const float t1 = fmaf(x1, cl2, -lv[e + 1]);
-            if (MODE == 0)
-              acc[t] = fmaxf(acc[t], fmaxf(t0, t1));
-            else
-              acc[t] += fast_exp2(t0) + fast_exp2(t1);
-          }
-        }
+        if (t > 0) epilogue(c[t - 1], L, t - 1, ks * 8 / KS, (ks + 1) * 8 / KS);
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
-    if (it + 1 < n_tiles) store_tile(buf ^ 1);
+    epilogue(c[NT - 1], L, NT - 1, 0, 8);
+    store_tile(buf ^ 1);
     __syncthreads();
   }
 
