@@ -33,7 +33,6 @@ namespace kvz {
 namespace {
 
 constexpr int KT = 32;          // keys per pass-1 tile
-constexpr int P1_ROWS = 256;    // query rows per pass-1 workgroup (4 waves x 64)
 constexpr float kNegBig = -1e30f;
 
 #ifndef KVZ_P1_TARGET_WGS
@@ -88,16 +87,25 @@ __device__ __forceinline__ float tile_sum(const f32x16& a, float m, float cl2) {
          (((e[8] + e[9]) + (e[10] + e[11])) + ((e[12] + e[13]) + (e[14] + e[15])));
 }
 
-// Commit the sums of both query columns of a lane; one branch for both so
-// that the two sums are computed before it (and overlap the MFMAs).
-__device__ __forceinline__ void lazy_commit2(const f32x16 (&a)[2], float s0, float s1,
-                                             float (&m)[2], float (&l)[2], float cl2) {
-  if (fmaxf(s0, s1) <= kLazyLimit) {
-    l[0] += s0;
-    l[1] += s1;
+// Commit the tile sums of a lane's NQ query columns; one branch for all so
+// that every sum is computed before it (and overlaps the MFMAs).
+template <int NQ>
+__device__ __forceinline__ void lazy_commit(const f32x16 (&a)[NQ], const float (&sm)[NQ],
+                                            float (&m)[NQ], float (&l)[NQ], float cl2) {
+  float big = sm[0];
+#pragma unroll
+  for (int t = 1; t < NQ; ++t) big = fmaxf(big, sm[t]);
+  if (big <= kLazyLimit) {
+#pragma unroll
+    for (int t = 0; t < NQ; ++t) l[t] += sm[t];
   } else {
-    if (s0 <= kLazyLimit) l[0] += s0; else online_update(a[0], m[0], l[0], cl2);
-    if (s1 <= kLazyLimit) l[1] += s1; else online_update(a[1], m[1], l[1], cl2);
+#pragma unroll
+    for (int t = 0; t < NQ; ++t) {
+      if (sm[t] <= kLazyLimit)
+        l[t] += sm[t];
+      else
+        online_update(a[t], m[t], l[t], cl2);
+    }
   }
 }
 
@@ -108,16 +116,25 @@ __device__ __forceinline__ int acc_row(int v, int half) {
 
 // ---------------------------------------------------------------------------
 // pass 1, bf16: partial (max, sum) per query row and key split
-// grid: H x splits x row-tiles (XCD-remapped: head-major, row tile fastest)
+// grid: H x splits x row tiles (XCD-remapped: head-major, row tile fastest)
 //
-// Main loop (tiles with no masked key): software-pipelined over 32-key
-// tiles.  Iteration t prefetches tile t+2 from global memory into registers,
-// issues the LDS reads and MFMAs of tile t+1 into one accumulator set and,
-// interleaved with them, the exp/sum work of tile t from the other set; it
-// then stores tile t+2 into the LDS buffer that tile t occupied.  One barrier
-// per tile.  Masked tiles (the ragged last context tile, the causal in-chunk
+// Each wave keeps NQ 32-row query tiles in registers (the B operand of
+// K*Q^T) and sweeps 32-key tiles of K staged in LDS; every A operand read
+// from LDS feeds NQ MFMAs.  Main loop (tiles with no masked key),
+// software-pipelined: iteration t prefetches tile t+2 from global memory,
+// issues the NQ*KS MFMAs of tile t+1 into one accumulator set and, between
+// them in a fixed order, the exp/sum work of tile t from the other set; then
+// it stores tile t+2 into the LDS buffer tile t occupied and passes one
+// barrier.  A operands are read AW k-steps ahead.  The online sum is lazy
+// (tile_sum).  Masked tiles (the ragged last context tile, the causal chunk
 // keys) take a simple unpipelined path.
 // ---------------------------------------------------------------------------
+template <int D>
+struct P1Shape {
+  static constexpr int NQ = 2;  // query tiles per wave
+  static constexpr int ROWS = 4 * 32 * NQ;                     // query rows per workgroup
+};
+
 template <int D>
 __global__ __launch_bounds__(256) void score_pass1_bf16(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ kc,
@@ -125,7 +142,9 @@ __global__ __launch_bounds__(256) void score_pass1_bf16(
     int R, int R_pad, int n_rt, int n_split_ctx, int tiles_per_split, float cl2,
     int n_blocks) {
   constexpr int KS = Geo<D>::KS, CH = Geo<D>::CH, SWZ = Geo<D>::SWZ;
+  constexpr int NQ = P1Shape<D>::NQ, ROWS = P1Shape<D>::ROWS;
   constexpr int LOADS = KT * CH / 256;
+  constexpr int AW = KS <= 8 ? KS : 4;  // A-operand k-steps held at once
   __shared__ uint4 lds[2][KT * CH];
 
   const int lb = xcd_logical_block();
@@ -151,18 +170,19 @@ __global__ __launch_bounds__(256) void score_pass1_bf16(
   } else {
     kbase = kin + (size_t)h * n_in * D;
     nkeys = n_in;
-    const int rlast = min(R, (rt + 1) * P1_ROWS) - 1;
+    const int rlast = min(R, (rt + 1) * ROWS) - 1;
     t_begin = 0;
     t_end = (rlast / G) / KT + 1;
     t_clean = t_begin;  // every in-chunk tile is causally masked
   }
 
-  // stationary query operand (B of K*Q^T): this lane's query column n
-  bf16x8 qr[2][KS];
-  int irow[2], grow[2];
+  // stationary query operand (B of K*Q^T): this lane's query column n of
+  // each of the wave's NQ row tiles
+  bf16x8 qr[NQ][KS];
+  int irow[NQ], grow[NQ];
 #pragma unroll
-  for (int t = 0; t < 2; ++t) {
-    const int r = rt * P1_ROWS + wave * 64 + t * 32 + n;
+  for (int t = 0; t < NQ; ++t) {
+    const int r = rt * ROWS + wave * (32 * NQ) + t * 32 + n;
     irow[t] = r / G;
     grow[t] = r - irow[t] * G;
     if (r < R) {
@@ -175,13 +195,26 @@ __global__ __launch_bounds__(256) void score_pass1_bf16(
     }
   }
 
-  float m[2] = {kNegBig, kNegBig}, l[2] = {0.f, 0.f};
+  float m[NQ], l[NQ];
+#pragma unroll
+  for (int t = 0; t < NQ; ++t) {
+    m[t] = kNegBig;
+    l[t] = 0.f;
+  }
   uint4 reg[LOADS];
   auto load_tile = [&](int tile) {
 #pragma unroll
     for (int u = 0; u < LOADS; ++u) {
       const int c = tid + 256 * u, row = c / CH, ch = c % CH, key = tile * KT + row;
       reg[u] = key < nkeys ? ld16(kbase + (size_t)key * D + ch * 8) : make_uint4(0, 0, 0, 0);
+    }
+  };
+  // tiles of the clean range hold KT valid keys: no bounds test, no branch
+  auto load_full = [&](int tile) {
+#pragma unroll
+    for (int u = 0; u < LOADS; ++u) {
+      const int c = tid + 256 * u, row = c / CH, ch = c % CH, key = tile * KT + row;
+      reg[u] = ld16(kbase + (size_t)key * D + ch * 8);
     }
   };
   auto store_tile = [&](int buf) {
@@ -191,85 +224,70 @@ __global__ __launch_bounds__(256) void score_pass1_bf16(
       lds[buf][swz<CH, SWZ>(row, ch)] = reg[u];
     }
   };
-  // tiles of the clean range hold KT valid keys: no bounds test, no branch
-  auto load_full = [&](int tile, uint4 (&r)[LOADS]) {
-#pragma unroll
-    for (int u = 0; u < LOADS; ++u) {
-      const int c = tid + 256 * u, row = c / CH, ch = c % CH, key = tile * KT + row;
-      r[u] = ld16(kbase + (size_t)key * D + ch * 8);
-    }
-  };
-  auto store_regs = [&](int buf, const uint4 (&r)[LOADS]) {
-#pragma unroll
-    for (int u = 0; u < LOADS; ++u) {
-      const int c = tid + 256 * u, row = c / CH, ch = c % CH;
-      lds[buf][swz<CH, SWZ>(row, ch)] = r[u];
-    }
-  };
-  auto mfma_tile = [&](int buf, f32x16 (&c)[2]) {
-    bf16x8 a[KS];
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) a[ks] = as_bf16x8(lds[buf][swz<CH, SWZ>(n, ks * 2 + half)]);
+  auto mfma_tile = [&](int buf, f32x16 (&c)[NQ]) {
     const f32x16 z = {};
-    c[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[0], qr[0][0], z, 0, 0, 0);
-    c[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[0], qr[1][0], z, 0, 0, 0);
 #pragma unroll
-    for (int ks = 1; ks < KS; ++ks) {
-      c[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[ks], qr[0][ks], c[0], 0, 0, 0);
-      c[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[ks], qr[1][ks], c[1], 0, 0, 0);
+    for (int ks = 0; ks < KS; ++ks) {
+      const bf16x8 a = as_bf16x8(lds[buf][swz<CH, SWZ>(n, ks * 2 + half)]);
+#pragma unroll
+      for (int t = 0; t < NQ; ++t)
+        c[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qr[t][ks], ks == 0 ? z : c[t], 0, 0, 0);
     }
   };
 
   const int nclean = t_clean - t_begin;
   if (nclean > 0) {
-    // Tile t lives in LDS buffer t & 1.  Iteration it: global loads of tile
-    // it+2, then 2*KS MFMAs of tile it+1, each preceded by an equal share of
-    // the exp/sum work of tile it (explicit order, fenced against the
-    // scheduler), then the LDS store of tile it+2 and one barrier.  Indices
-    // past the range re-load the last tile; those copies are never consumed.
-    constexpr int NCH = 2 * KS;      // one chunk of VALU work per MFMA
-    constexpr int PER = 32 / NCH;    // logits per chunk (2 columns x 16)
-    f32x16 A[2], B[2];
+    // Tile t lives in LDS buffer t & 1.  Indices past the range re-load the
+    // last tile; those copies are never consumed.
+    constexpr int NCH = NQ * KS;      // one chunk of VALU work per MFMA
+    f32x16 A[NQ], B[NQ];
     const int last = nclean - 1;
-    load_full(t_begin, reg);
-    store_regs(0, reg);
+    load_full(t_begin);
+    store_tile(0);
     __syncthreads();
-    load_full(t_begin + min(1, last), reg);
+    load_full(t_begin + min(1, last));
     mfma_tile(0, A);
-    store_regs(1, reg);
+    store_tile(1);
     __syncthreads();
-    auto body = [&](int it, f32x16 (&cur)[2], f32x16 (&nxt)[2]) {
-      load_full(t_begin + min(it + 2, last), reg);
+    auto body = [&](int it, f32x16 (&cur)[NQ], f32x16 (&nxt)[NQ]) {
+      load_full(t_begin + min(it + 2, last));
       const int buf = (it + 1) & 1;
-      bf16x8 a[KS];
+      bf16x8 a[AW];
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks)
+      for (int ks = 0; ks < AW; ++ks)
         a[ks] = as_bf16x8(lds[buf][swz<CH, SWZ>(n, ks * 2 + half)]);
       __builtin_amdgcn_sched_barrier(0);
       const f32x16 z = {};
-      float sm[2][4];
+      float sm[NQ][4];
 #pragma unroll
       for (int c = 0; c < NCH; ++c) {
+        // logits e of this chunk: 16*NQ per lane spread over the NCH chunks
 #pragma unroll
-        for (int e = c * PER; e < (c + 1) * PER; ++e) {
+        for (int e = c * 16 / KS; e < (c + 1) * 16 / KS; ++e) {
           const int col = e >> 4, v = e & 15;
           const float x = fast_exp2(fmaf(cur[col][v], cl2, -m[col]));
           if (v < 4) sm[col][v] = x; else sm[col][v & 3] += x;
         }
         __builtin_amdgcn_sched_barrier(0);
-        const int ks = c >> 1, t = c & 1;
-        nxt[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[ks], qr[t][ks], ks == 0 ? z : nxt[t],
-                                                         0, 0, 0);
+        const int ks = c / NQ, t = c % NQ;
+        nxt[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[ks % AW], qr[t][ks],
+                                                         ks == 0 ? z : nxt[t], 0, 0, 0);
+        if (t == NQ - 1 && ks + AW < KS)
+          a[ks % AW] = as_bf16x8(lds[buf][swz<CH, SWZ>(n, (ks + AW) * 2 + half)]);
         __builtin_amdgcn_sched_barrier(0);
       }
-      const float s0 = (sm[0][0] + sm[0][1]) + (sm[0][2] + sm[0][3]);
-      const float s1 = (sm[1][0] + sm[1][1]) + (sm[1][2] + sm[1][3]);
-      lazy_commit2(cur, s0, s1, m, l, cl2);
-      store_regs(it & 1, reg);
+      float tot[NQ];
+#pragma unroll
+      for (int t = 0; t < NQ; ++t) tot[t] = (sm[t][0] + sm[t][1]) + (sm[t][2] + sm[t][3]);
+      lazy_commit<NQ>(cur, tot, m, l, cl2);
+      store_tile(it & 1);
       __syncthreads();
     };
-    auto finish = [&](f32x16 (&cur)[2]) {
-      lazy_commit2(cur, tile_sum(cur[0], m[0], cl2), tile_sum(cur[1], m[1], cl2), m, l, cl2);
+    auto finish = [&](f32x16 (&cur)[NQ]) {
+      float tot[NQ];
+#pragma unroll
+      for (int t = 0; t < NQ; ++t) tot[t] = tile_sum(cur[t], m[t], cl2);
+      lazy_commit<NQ>(cur, tot, m, l, cl2);
     };
     int it = 0;
     for (; it + 2 < nclean; it += 2) {
@@ -290,28 +308,28 @@ __global__ __launch_bounds__(256) void score_pass1_bf16(
     load_tile(tile);
     store_tile(0);
     __syncthreads();
-    f32x16 c[2];
+    f32x16 c[NQ];
     mfma_tile(0, c);
     const int key0 = tile * KT;
 #pragma unroll
     for (int v = 0; v < 16; ++v) {
       const int key = key0 + acc_row(v, half);
-      const bool bad = inchunk ? false : key >= n_c;
-      if (bad || (inchunk && key > irow[0])) c[0][v] = -INFINITY;
-      if (bad || (inchunk && key > irow[1])) c[1][v] = -INFINITY;
+#pragma unroll
+      for (int t = 0; t < NQ; ++t)
+        if (inchunk ? key > irow[t] : key >= n_c) c[t][v] = -INFINITY;
     }
-    online_update(c[0], m[0], l[0], cl2);
-    online_update(c[1], m[1], l[1], cl2);
+#pragma unroll
+    for (int t = 0; t < NQ; ++t) online_update(c[t], m[t], l[t], cl2);
   }
 
   // lanes n and n+32 hold the same query column, different key rows
 #pragma unroll
-  for (int t = 0; t < 2; ++t) {
+  for (int t = 0; t < NQ; ++t) {
     const float mo = __shfl_xor(m[t], 32);
     const float lo = __shfl_xor(l[t], 32);
     const float M = fmaxf(m[t], mo);
     const float L = l[t] * fast_exp2(m[t] - M) + lo * fast_exp2(mo - M);
-    const int r = rt * P1_ROWS + wave * 64 + t * 32 + n;
+    const int r = rt * ROWS + wave * (32 * NQ) + t * 32 + n;
     if (half == 0 && r < R) {
       // partials and lse are stored in g-major row order (g * n_in + i)
       part[((size_t)h * splits + s) * R_pad + grow[t] * n_in + irow[t]] = make_float2(M, L);
@@ -652,8 +670,10 @@ ScorePlan score_plan(kvz_dtype dt, int H, int G, int n_in, int d, int n_c) {
   p.n_c = n_c;
   p.n_in = n_in;
   p.R = G * n_in;
-  p.n_rt = (p.R + P1_ROWS - 1) / P1_ROWS;
-  p.R_pad = p.n_rt * P1_ROWS;
+  const int rows = d == 64 ? P1Shape<64>::ROWS : d == 128 ? P1Shape<128>::ROWS
+                                                            : P1Shape<256>::ROWS;
+  p.n_rt = (p.R + rows - 1) / rows;
+  p.R_pad = p.n_rt * rows;  // a multiple of 32 (the pass-2 row tile)
   const int n_ctx_tiles = (n_c + KT - 1) / KT;
   if (dt == KVZ_BF16) {
     // enough workgroups to cover the chip a few times, at least 16 tiles each
