@@ -37,6 +37,28 @@ __device__ __forceinline__ bf16x8 as_bf16x8(uint4 u) {
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
 
+// Word 3 of a raw buffer resource on gfx9-family parts: 32-bit data format
+// (a zero format makes buffer loads return zero), no swizzle, no index
+// stride.  With stride 0 the hardware range check is offset < num_records
+// bytes; loads outside return zero and touch no memory.
+constexpr int kBufferFlags = 0x00020000;
+
+// LDS address-space view of a __shared__ object (the LDS destination of a
+// buffer load with the lds flag is a wave-uniform base in M0; lane i writes
+// base + 16*i for a 16-byte load).
+__device__ __forceinline__ __attribute__((address_space(3))) void* lds_ptr(void* p) {
+  return (__attribute__((address_space(3))) void*)(p);
+}
+
+// Each lane of the wave copies the 16 bytes at base + voff into LDS at
+// dst + 16*lane (dst wave-uniform).  base..base+nbytes is the buffer's range:
+// offsets outside it read as zero.  The copy is counted by vmcnt.
+__device__ __forceinline__ void copy16_to_lds(const void* base, int nbytes, int voff, void* dst) {
+  const __amdgpu_buffer_rsrc_t r =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, nbytes, kBufferFlags);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, lds_ptr(dst), 16, voff, 0, 0, 0);
+}
+
 // ---------------------------------------------------------------------------
 // host side: launch timing hooks (see kvz_prof_enable in kvz.h)
 // ---------------------------------------------------------------------------

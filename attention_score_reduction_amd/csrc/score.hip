@@ -109,6 +109,15 @@ __device__ __forceinline__ void lazy_commit(const f32x16 (&a)[NQ], const float (
   }
 }
 
+// Pass-1 exp work of one tile, NE logits per lane, spread over the NCH MFMAs
+// of the next tile: chunk c (the VALU work issued before MFMA c) takes logits
+// [chunk_lo(c), chunk_lo(c+1)).  Chunk 0 takes a quarter of them, so the first
+// MFMA's wait for its LDS operand is covered; the rest are spread evenly.
+template <int NE, int NCH>
+__device__ constexpr int chunk_lo(int c) {
+  return c <= 0 ? 0 : NE / 4 + (c - 1) * (NE - NE / 4) / (NCH - 1);
+}
+
 // Row index (within a 32x32 MFMA output tile) held by accumulator v of a lane.
 __device__ __forceinline__ int acc_row(int v, int half) {
   return 8 * (v >> 2) + 4 * half + (v & 3);
@@ -121,13 +130,14 @@ __device__ __forceinline__ int acc_row(int v, int half) {
 // Each wave keeps NQ 32-row query tiles in registers (the B operand of
 // K*Q^T) and sweeps 32-key tiles of K staged in LDS; every A operand read
 // from LDS feeds NQ MFMAs.  Main loop (tiles with no masked key),
-// software-pipelined: iteration t prefetches tile t+2 from global memory,
-// issues the NQ*KS MFMAs of tile t+1 into one accumulator set and, between
-// them in a fixed order, the exp/sum work of tile t from the other set; then
-// it stores tile t+2 into the LDS buffer tile t occupied and passes one
-// barrier.  A operands are read AW k-steps ahead.  The online sum is lazy
-// (tile_sum).  Masked tiles (the ragged last context tile, the causal chunk
-// keys) take a simple unpipelined path.
+// software-pipelined: iteration t reads its first A operands of tile t+1,
+// starts the global -> LDS copy of tile t+2 into the buffer tile t occupied
+// (buffer loads with an LDS destination: no register staging), issues the
+// NQ*KS MFMAs of tile t+1 into one accumulator set and, between them in a
+// fixed order, the exp/sum work of tile t from the other set; then it waits
+// for its copies and passes one barrier.  A operands are read AW k-steps
+// ahead.  The online sum is lazy (tile_sum).  Masked tiles (the ragged last
+// context tile, the causal chunk keys) take a simple unpipelined path.
 // ---------------------------------------------------------------------------
 template <int D>
 struct P1Shape {
@@ -145,7 +155,7 @@ __global__ __launch_bounds__(256) void score_pass1_bf16(
   constexpr int NQ = P1Shape<D>::NQ, ROWS = P1Shape<D>::ROWS;
   constexpr int LOADS = KT * CH / 256;
   constexpr int AW = KS <= 8 ? KS : 4;  // A-operand k-steps held at once
-  __shared__ uint4 lds[2][KT * CH];
+  __shared__ uint4 lds0[KT * CH], lds1[KT * CH];
 
   const int lb = xcd_logical_block();
   if (lb >= n_blocks) return;
@@ -201,6 +211,9 @@ __global__ __launch_bounds__(256) void score_pass1_bf16(
     m[t] = kNegBig;
     l[t] = 0.f;
   }
+  // LDS buffers of the K tiles, as two objects so that the copy into one
+  // is never taken to alias the operand reads from the other
+  auto ldsb = [&](int b) -> uint4* { return b ? lds1 : lds0; };
   uint4 reg[LOADS];
   auto load_tile = [&](int tile) {
 #pragma unroll
@@ -209,26 +222,18 @@ __global__ __launch_bounds__(256) void score_pass1_bf16(
       reg[u] = key < nkeys ? ld16(kbase + (size_t)key * D + ch * 8) : make_uint4(0, 0, 0, 0);
     }
   };
-  // tiles of the clean range hold KT valid keys: no bounds test, no branch
-  auto load_full = [&](int tile) {
-#pragma unroll
-    for (int u = 0; u < LOADS; ++u) {
-      const int c = tid + 256 * u, row = c / CH, ch = c % CH, key = tile * KT + row;
-      reg[u] = ld16(kbase + (size_t)key * D + ch * 8);
-    }
-  };
   auto store_tile = [&](int buf) {
 #pragma unroll
     for (int u = 0; u < LOADS; ++u) {
       const int c = tid + 256 * u, row = c / CH, ch = c % CH;
-      lds[buf][swz<CH, SWZ>(row, ch)] = reg[u];
+      ldsb(buf)[swz<CH, SWZ>(row, ch)] = reg[u];
     }
   };
   auto mfma_tile = [&](int buf, f32x16 (&c)[NQ]) {
     const f32x16 z = {};
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-      const bf16x8 a = as_bf16x8(lds[buf][swz<CH, SWZ>(n, ks * 2 + half)]);
+      const bf16x8 a = as_bf16x8(ldsb(buf)[swz<CH, SWZ>(n, ks * 2 + half)]);
 #pragma unroll
       for (int t = 0; t < NQ; ++t)
         c[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qr[t][ks], ks == 0 ? z : c[t], 0, 0, 0);
@@ -237,50 +242,81 @@ __global__ __launch_bounds__(256) void score_pass1_bf16(
 
   const int nclean = t_clean - t_begin;
   if (nclean > 0) {
-    // Tile t lives in LDS buffer t & 1.  Indices past the range re-load the
-    // last tile; those copies are never consumed.
+    // Tile t (relative to t_begin) lives in LDS buffer t & 1.  Tiles of the
+    // clean range go global -> LDS by buffer loads with an LDS destination:
+    // one such load fills 64 consecutive 16-byte slots, one per lane, so each
+    // lane fetches the (key, chunk) that the swizzled layout puts in its slot.
+    // Indices past the range re-copy the last tile; those copies are never
+    // consumed.
     constexpr int NCH = NQ * KS;      // one chunk of VALU work per MFMA
+    constexpr int NE = 16 * NQ;       // logits per lane per tile
     f32x16 A[NQ], B[NQ];
     const int last = nclean - 1;
-    load_full(t_begin);
-    store_tile(0);
+    const uint16_t* kseg = kbase + (size_t)t_begin * KT * D;
+    const int seg_bytes = (nkeys - t_begin * KT) * D * 2;
+    int koff[LOADS];
+#pragma unroll
+    for (int u = 0; u < LOADS; ++u) {
+      const int slot = (u * 4 + wave) * 64 + lane;
+      const int row = slot / CH, ch = (slot % CH) ^ (row & SWZ);
+      koff[u] = row * D * 2 + ch * 16;
+    }
+    auto copy_tile = [&](int rt_, int buf) {
+#pragma unroll
+      for (int u = 0; u < LOADS; ++u)
+        copy16_to_lds(kseg, seg_bytes, koff[u] + rt_ * (KT * D * 2), ldsb(buf) + (u * 4 + wave) * 64);
+    };
+    copy_tile(0, 0);
+    copy_tile(min(1, last), 1);
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    load_full(t_begin + min(1, last));
     mfma_tile(0, A);
-    store_tile(1);
-    __syncthreads();
-    auto body = [&](int it, f32x16 (&cur)[NQ], f32x16 (&nxt)[NQ]) {
-      load_full(t_begin + min(it + 2, last));
-      const int buf = (it + 1) & 1;
+    __syncthreads();  // every wave has read buffer 0 before it is refilled
+    // iteration it (parity par = it & 1, a literal at each call): MFMAs of
+    // tile it+1, exp/sum work of tile it, copy of tile it+2 into the buffer
+    // tile it occupied
+    auto body = [&](int it, f32x16 (&cur)[NQ], f32x16 (&nxt)[NQ], int par) {
+      const int buf = par ^ 1;
       bf16x8 a[AW];
 #pragma unroll
       for (int ks = 0; ks < AW; ++ks)
-        a[ks] = as_bf16x8(lds[buf][swz<CH, SWZ>(n, ks * 2 + half)]);
+        a[ks] = as_bf16x8(ldsb(buf)[swz<CH, SWZ>(n, ks * 2 + half)]);
+      copy_tile(min(it + 2, last), par);
       __builtin_amdgcn_sched_barrier(0);
       const f32x16 z = {};
-      float sm[NQ][4];
+      float sm[NQ][4], ex[NE];
+      // the sums take each exp one chunk after it is formed, so no add
+      // waits on the exp just issued
+      auto add_chunk = [&](int c) {
+#pragma unroll
+        for (int e = chunk_lo<NE, NCH>(c); e < chunk_lo<NE, NCH>(c + 1); ++e) {
+          const int col = e >> 4, v = e & 15;
+          if (v < 4) sm[col][v] = ex[e]; else sm[col][v & 3] += ex[e];
+        }
+      };
 #pragma unroll
       for (int c = 0; c < NCH; ++c) {
-        // logits e of this chunk: 16*NQ per lane spread over the NCH chunks
+        // logits [chunk_lo(c), chunk_lo(c+1)) of this lane's 16*NQ
 #pragma unroll
-        for (int e = c * 16 / KS; e < (c + 1) * 16 / KS; ++e) {
+        for (int e = chunk_lo<NE, NCH>(c); e < chunk_lo<NE, NCH>(c + 1); ++e) {
           const int col = e >> 4, v = e & 15;
-          const float x = fast_exp2(fmaf(cur[col][v], cl2, -m[col]));
-          if (v < 4) sm[col][v] = x; else sm[col][v & 3] += x;
+          ex[e] = fast_exp2(fmaf(cur[col][v], cl2, -m[col]));
         }
+        if (c > 0) add_chunk(c - 1);
         __builtin_amdgcn_sched_barrier(0);
         const int ks = c / NQ, t = c % NQ;
         nxt[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[ks % AW], qr[t][ks],
                                                          ks == 0 ? z : nxt[t], 0, 0, 0);
         if (t == NQ - 1 && ks + AW < KS)
-          a[ks % AW] = as_bf16x8(lds[buf][swz<CH, SWZ>(n, (ks + AW) * 2 + half)]);
+          a[ks % AW] = as_bf16x8(ldsb(buf)[swz<CH, SWZ>(n, (ks + AW) * 2 + half)]);
         __builtin_amdgcn_sched_barrier(0);
       }
+      add_chunk(NCH - 1);
       float tot[NQ];
 #pragma unroll
       for (int t = 0; t < NQ; ++t) tot[t] = (sm[t][0] + sm[t][1]) + (sm[t][2] + sm[t][3]);
       lazy_commit<NQ>(cur, tot, m, l, cl2);
-      store_tile(it & 1);
+      __builtin_amdgcn_s_waitcnt(0);  // this wave's copy of tile it+2 has landed
       __syncthreads();
     };
     auto finish = [&](f32x16 (&cur)[NQ]) {
@@ -291,11 +327,11 @@ __global__ __launch_bounds__(256) void score_pass1_bf16(
     };
     int it = 0;
     for (; it + 2 < nclean; it += 2) {
-      body(it, A, B);
-      body(it + 1, B, A);
+      body(it, A, B, 0);
+      body(it + 1, B, A, 1);
     }
     if (it + 1 < nclean) {
-      body(it, A, B);
+      body(it, A, B, 0);
       finish(B);
     } else {
       finish(A);
@@ -387,8 +423,11 @@ __global__ __launch_bounds__(256) void score_pass2_bf16(
   constexpr int KS = Geo<D>::KS, CH = Geo<D>::CH, SWZ = Geo<D>::SWZ;
   constexpr int NT = P2Shape<D>::NT;
   constexpr int RT = 32;                     // query rows per tile
-  constexpr int LOADS = RT * CH / 256;
+  constexpr int LOADS = RT * CH / 256;       // 16-byte copies per thread per tile
   __shared__ uint4 ldq[2][RT * CH];
+  // the tile's 32 row lse values (8 float4); 64 slots, one per lane of the
+  // copying wave, although only 8 lanes copy
+  __shared__ float4 ldl[2][64];
 
   const int lb = xcd_logical_block();
   if (lb >= n_blocks) return;
@@ -409,23 +448,27 @@ __global__ __launch_bounds__(256) void score_pass2_bf16(
     for (int ks = 0; ks < KS; ++ks) kr[t][ks] = as_bf16x8(ld16(p + ks * 16));
   }
 
-  const float* lseh = lse2 + (size_t)h * R_pad;
-  const uint16_t* qh = q + (size_t)h * R * D;  // rows of head h, g-major: g * n_in + i
+  // Query tiles go global -> LDS by buffer loads with an LDS destination (no
+  // register staging).  One such load writes 64 consecutive 16-byte LDS slots,
+  // one per lane, so each lane fetches the (row, chunk) that the swizzled
+  // layout puts in its slot.  The buffer covers the R rows of head h: padding
+  // rows (r >= R) fall outside it and read as zero (they carry lse = +inf).
   const int n_tiles = R_pad / RT;
-  uint4 reg[LOADS];
-  auto load_tile = [&](int t) {
+  const uint16_t* qh = q + (size_t)h * R * D;
+  const float* lseh = lse2 + (size_t)h * R_pad;
+  int qoff[LOADS];
 #pragma unroll
-    for (int u = 0; u < LOADS; ++u) {
-      const int c = tid + 256 * u, row = c / CH, ch = c % CH, rr = min(t * RT + row, R - 1);
-      reg[u] = ld16(qh + (size_t)rr * D + ch * 8);
-    }
-  };
-  auto store_tile = [&](int buf) {
+  for (int u = 0; u < LOADS; ++u) {
+    const int slot = (u * 4 + wave) * 64 + lane;
+    const int row = slot / CH, ch = (slot % CH) ^ (row & SWZ);
+    qoff[u] = row * D * 2 + ch * 16;
+  }
+  auto copy_tile = [&](int t, int buf) {
 #pragma unroll
-    for (int u = 0; u < LOADS; ++u) {
-      const int c = tid + 256 * u, row = c / CH, ch = c % CH;
-      ldq[buf][swz<CH, SWZ>(row, ch)] = reg[u];
-    }
+    for (int u = 0; u < LOADS; ++u)
+      copy16_to_lds(qh, R * D * 2, qoff[u] + t * (RT * D * 2), &ldq[buf][(u * 4 + wave) * 64]);
+    if (MODE != 2 && wave == 0 && lane < RT / 4)
+      copy16_to_lds(lseh, R_pad * 4, (t * RT + 4 * lane) * 4, &ldl[buf][0]);
   };
 
   const float init = MODE == 1 ? 0.f : -INFINITY;
@@ -440,38 +483,36 @@ __global__ __launch_bounds__(256) void score_pass2_bf16(
       const int v = 2 * pr;
       const float x0 = c[v], x1 = c[v + 1];
       if (MODE == 2) {
-        acc[t] = fmaxf(acc[t], fmaxf(x0, x1));
+        acc[t] = fmaxf(fmaxf(acc[t], x0), x1);
       } else {
         const float4 L4 = L[v >> 2];
         const float l0 = (v & 3) == 0 ? L4.x : L4.z, l1 = (v & 3) == 0 ? L4.y : L4.w;
         const float t0 = fmaf(x0, cl2, -l0);
         const float t1 = fmaf(x1, cl2, -l1);
         if (MODE == 0)
-          acc[t] = fmaxf(acc[t], fmaxf(t0, t1));
+          acc[t] = fmaxf(fmaxf(acc[t], t0), t1);
         else
           acc[t] += fast_exp2(t0) + fast_exp2(t1);
       }
     }
   };
 
-  load_tile(0);
-  store_tile(0);
-  __syncthreads();
-  for (int it = 0; it < n_tiles; ++it) {
-    const int buf = it & 1;
-    // the last iteration re-loads and re-stores its own tile into the idle
-    // buffer (never read again): no branch in the loop body
-    load_tile(min(it + 1, n_tiles - 1));
-    // lse of the 16 rows this lane holds in the MFMA output
+  // one query tile: read this tile's operands from LDS, start the copy of the
+  // next tile into the idle buffer, MFMAs and epilogues, then wait for this
+  // wave's copies and pass the barrier.  The last tile re-copies itself into the idle buffer (never
+  // read again): no branch in the body.
+  auto body = [&](int it, int buf) {
+    // lse of the 16 rows this lane holds in the MFMA output (rows 8*vg + 4*half + 0..3)
     float4 L[4];
     if (MODE != 2) {
 #pragma unroll
-      for (int vg = 0; vg < 4; ++vg)
-        L[vg] = *reinterpret_cast<const float4*>(lseh + it * RT + 8 * vg + 4 * half);
+      for (int vg = 0; vg < 4; ++vg) L[vg] = ldl[buf][2 * vg + half];
     }
     bf16x8 a[KS];
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) a[ks] = as_bf16x8(ldq[buf][swz<CH, SWZ>(n, ks * 2 + half)]);
+    // issued after this tile's LDS reads, so that no read waits for the copy
+    copy_tile(min(it + 1, n_tiles - 1), buf ^ 1);
     f32x16 c[NT];
     const f32x16 z = {};
     __builtin_amdgcn_sched_barrier(0);
@@ -487,9 +528,14 @@ __global__ __launch_bounds__(256) void score_pass2_bf16(
       }
     }
     epilogue(c[NT - 1], L, NT - 1, 0, 8);
-    store_tile(buf ^ 1);
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-  }
+  };
+
+  copy_tile(0, 0);
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  for (int it = 0; it < n_tiles; ++it) body(it, it & 1);
 
 #pragma unroll
   for (int t = 0; t < NT; ++t) {
