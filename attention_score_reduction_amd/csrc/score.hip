@@ -373,16 +373,17 @@ __global__ __launch_bounds__(256) void score_pass1_bf16(
   }
 }
 
-// merge the key splits: lse2 = M + log2(sum_s l_s 2^(m_s - M)); padding rows
-// get +inf so that pass 2 ignores them.
+// merge the key splits: lse2 = M + log2(sum_s l_s 2^(m_s - M)), written
+// times mul (1, or -1/(scale log2 e) when pass 2 takes it in raw dot-product
+// units); padding rows get +inf * mul so that pass 2 ignores them.
 __global__ __launch_bounds__(256) void score_combine(const float2* __restrict__ part,
                                                      float* __restrict__ lse2, int splits,
-                                                     int R, int R_pad, int H) {
+                                                     int R, int R_pad, int H, float mul) {
   const int idx = blockIdx.x * 256 + threadIdx.x;
   if (idx >= H * R_pad) return;
   const int h = idx / R_pad, r = idx - h * R_pad;
   if (r >= R) {
-    lse2[idx] = INFINITY;
+    lse2[idx] = INFINITY * mul;
     return;
   }
   const float2* p = part + (size_t)h * splits * R_pad + r;
@@ -393,7 +394,7 @@ __global__ __launch_bounds__(256) void score_combine(const float2* __restrict__ 
     const float2 v = p[(size_t)s * R_pad];
     L += v.y * exp2f(v.x - M);
   }
-  lse2[idx] = M + log2f(L);
+  lse2[idx] = (M + log2f(L)) * mul;
 }
 
 // ---------------------------------------------------------------------------
@@ -476,23 +477,22 @@ __global__ __launch_bounds__(256) void score_pass2_bf16(
 #pragma unroll
   for (int t = 0; t < NT; ++t) acc[t] = init;
 
-  // epilogue of one key tile: elements 2p, 2p+1 for p in [p0, p1)
+  // epilogue of one key tile: elements 2p, 2p+1 for p in [p0, p1).  MODE 0
+  // and 2 need only a running max: for MODE 0 the MFMA accumulator starts at
+  // -lse2/(scale log2 e) of its row, so its output is already the row's
+  // log-probability in dot-product units, and the scaling waits until after
+  // the max (it is positive).
   auto epilogue = [&](const f32x16& c, const float4 (&L)[4], int t, int p0, int p1) {
 #pragma unroll
     for (int pr = p0; pr < p1; ++pr) {
       const int v = 2 * pr;
       const float x0 = c[v], x1 = c[v + 1];
-      if (MODE == 2) {
+      if (MODE != 1) {
         acc[t] = fmaxf(fmaxf(acc[t], x0), x1);
       } else {
         const float4 L4 = L[v >> 2];
         const float l0 = (v & 3) == 0 ? L4.x : L4.z, l1 = (v & 3) == 0 ? L4.y : L4.w;
-        const float t0 = fmaf(x0, cl2, -l0);
-        const float t1 = fmaf(x1, cl2, -l1);
-        if (MODE == 0)
-          acc[t] = fmaxf(fmaxf(acc[t], t0), t1);
-        else
-          acc[t] += fast_exp2(t0) + fast_exp2(t1);
+        acc[t] += fast_exp2(fmaf(x0, cl2, -l0)) + fast_exp2(fmaf(x1, cl2, -l1));
       }
     }
   };
@@ -513,8 +513,14 @@ __global__ __launch_bounds__(256) void score_pass2_bf16(
     for (int ks = 0; ks < KS; ++ks) a[ks] = as_bf16x8(ldq[buf][swz<CH, SWZ>(n, ks * 2 + half)]);
     // issued after this tile's LDS reads, so that no read waits for the copy
     copy_tile(min(it + 1, n_tiles - 1), buf ^ 1);
-    f32x16 c[NT];
-    const f32x16 z = {};
+    f32x16 c[NT], z;
+    if (MODE == 0) {
+      // accumulator start: -lse2/(scale log2 e) of the lane's 16 rows
+#pragma unroll
+      for (int v = 0; v < 16; ++v) z[v] = L[v >> 2][v & 3];
+    } else {
+      z = f32x16{};
+    }
     __builtin_amdgcn_sched_barrier(0);
     // MFMAs of key tile t, each followed by a share of key tile t-1's epilogue
 #pragma unroll
@@ -546,7 +552,7 @@ __global__ __launch_bounds__(256) void score_pass2_bf16(
     if (half == 0 && j < n_c) {
       float* sp = S + (size_t)h * n_c + j;
       if (MODE == 0)
-        *sp = fmaxf(*sp, fminf(fast_exp2(r), 1.0f));
+        *sp = fmaxf(*sp, fminf(fast_exp2(r * cl2), 1.0f));
       else if (MODE == 1)
         *sp += r;
       else
@@ -661,7 +667,7 @@ hipError_t launch_bf16(const ScorePlan& p, const void* q, const void* kc, const 
                p.n_in, p.R, p.R_pad, p.n_rt, p.n_split_ctx, p.tiles_per_split, cl2, nb1);
     const int nc = p.H * p.R_pad;
     KVZ_LAUNCH("score_combine", score_combine, (nc + 255) / 256, 256, 0, st, part, lse2, splits,
-               p.R, p.R_pad, p.H);
+               p.R, p.R_pad, p.H, MODE == 0 ? -1.0f / cl2 : 1.0f);
   }
   const int n_kt = (p.n_c + P2Shape<D>::KEYS - 1) / P2Shape<D>::KEYS;
   const int nb2 = p.H * n_kt;
