@@ -285,8 +285,21 @@ __global__ __launch_bounds__(256) void score_pass1_bf16(
       __builtin_amdgcn_sched_barrier(0);
       const f32x16 z = {};
       float sm[NQ][4], ex[NE];
-      // the sums take each exp one chunk after it is formed, so no add
-      // waits on the exp just issued
+      // three-stage VALU pipeline over the chunks: the fma of a logit is
+      // issued one chunk (one MFMA) before its exp, and its add one chunk
+      // after, so no VALU op waits on the result of the op just before it
+      auto fma_chunk = [&](int c) {
+#pragma unroll
+        for (int e = chunk_lo<NE, NCH>(c); e < chunk_lo<NE, NCH>(c + 1); ++e) {
+          const int col = e >> 4, v = e & 15;
+          ex[e] = fmaf(cur[col][v], cl2, -m[col]);
+        }
+      };
+      auto exp_chunk = [&](int c) {
+#pragma unroll
+        for (int e = chunk_lo<NE, NCH>(c); e < chunk_lo<NE, NCH>(c + 1); ++e)
+          ex[e] = fast_exp2(ex[e]);
+      };
       auto add_chunk = [&](int c) {
 #pragma unroll
         for (int e = chunk_lo<NE, NCH>(c); e < chunk_lo<NE, NCH>(c + 1); ++e) {
@@ -294,14 +307,12 @@ __global__ __launch_bounds__(256) void score_pass1_bf16(
           if (v < 4) sm[col][v] = ex[e]; else sm[col][v & 3] += ex[e];
         }
       };
+      fma_chunk(0);
 #pragma unroll
       for (int c = 0; c < NCH; ++c) {
         // logits [chunk_lo(c), chunk_lo(c+1)) of this lane's 16*NQ
-#pragma unroll
-        for (int e = chunk_lo<NE, NCH>(c); e < chunk_lo<NE, NCH>(c + 1); ++e) {
-          const int col = e >> 4, v = e & 15;
-          ex[e] = fast_exp2(fmaf(cur[col][v], cl2, -m[col]));
-        }
+        exp_chunk(c);
+        if (c + 1 < NCH) fma_chunk(c + 1);
         if (c > 0) add_chunk(c - 1);
         __builtin_amdgcn_sched_barrier(0);
         const int ks = c / NQ, t = c % NQ;

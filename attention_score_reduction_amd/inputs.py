@@ -33,7 +33,7 @@ BF16 = "bf16"
 F32 = "f32"
 
 # tensor ids for the seed sequence
-_T_QUERY, _T_KCTX, _T_VCTX, _T_KIN, _T_FACTOR, _T_PEAK = range(6)
+_T_QUERY, _T_KCTX, _T_VCTX, _T_KIN, _T_FACTOR, _T_PEAK, _T_VIN = range(7)
 
 
 @dataclasses.dataclass(frozen=True)
@@ -166,6 +166,15 @@ class HostGen:
         kin = rk.standard_normal((wl.heads, n_in, wl.head_dim), dtype=np.float32)
         kin *= f[:, None, None]
         return self._store(q[hs]), self._store(kin[hs])
+
+    def chunk_values(self, layer, k, heads=None):
+        """V_in [H][n_in][d] of chunk k of one layer (the values of the
+        repeat-prompt and copied-context tokens), N(0, 1) like V_c."""
+        wl = self.wl
+        hs = list(range(wl.heads)) if heads is None else list(heads)
+        rv = self._rng(layer, _T_VIN, k)
+        vin = rv.standard_normal((wl.heads, wl.n_in(k), wl.head_dim), dtype=np.float32)
+        return self._store(vin[hs])
 
 
 def device_tensors(wl: Workload, device="cuda", layers=None):

@@ -133,6 +133,33 @@ def score_chunk(q, k_ctx, k_in, scale, S, row_block=256, mode="max"):
     return S
 
 
+def chunk_attention_output(q, k_ctx, k_in, v_ctx, v_in, scale, row_block=256):
+    """Output of the reconstruction attention of one chunk: every query row's
+    softmax over its visible keys applied to their values.
+
+    The scoring stage is a full forward of the model over [repeat prompt;
+    chunk] ([rebuttal] computational analysis: one MLP pass and two times the
+    prefill's attention work), so each layer's attention also produces
+    O = P [V_c ; V_in] for the layer above; a FlashAttention kernel returns
+    exactly this product and nothing else ([blog] 4.4).
+
+    q: [H][G][n_in][d], k_ctx, v_ctx: [H][n_c][d], k_in, v_in: [H][n_in][d],
+    all float64.  Returns O: [H][G][n_in][d] with
+    O[h, g, i] = sum_j P_{h,g}[i, j] * [v_ctx[h]; v_in[h]][j].
+    """
+    H, G, n_in, _ = q.shape
+    dv = v_ctx.shape[2]
+    O = np.zeros((H, G, n_in, dv))
+    for h in range(H):
+        vals = np.concatenate([v_ctx[h], v_in[h]], axis=0)      # [n_c + n_in][dv]
+        for g in range(G):
+            for r0 in range(0, n_in, row_block):
+                rows = np.arange(r0, min(n_in, r0 + row_block))
+                P = chunk_probabilities(q[h, g], k_ctx[h], k_in[h], scale, rows)
+                O[h, g, rows] = P @ vals
+    return O
+
+
 def score_layer(chunks, k_ctx, scale, mode="max"):
     """Scores of one layer from a list of chunks [(q, k_in), ...], S starting
     at 0 (max and sum of probabilities) or -inf (raw logits)."""

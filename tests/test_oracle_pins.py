@@ -391,3 +391,84 @@ def test_decode_attention_library_and_closed_forms():
     out2 = ras.decode_attention(q, k[:3], v[:3], offs2, 0.5)
     np.testing.assert_allclose(out2[0], np.broadcast_to(v[0], (G, d)), rtol=0, atol=0)
     assert np.all(out2[1] == 0.0)
+
+
+# ---------------------------------------------------------------------------
+# reconstruction attention output O = P [V_c; V_in]
+# ---------------------------------------------------------------------------
+
+def test_attention_output_closed_forms():
+    """V = ones gives O = 1 (rows of P sum to 1); Q = 0 gives O_i = the mean
+    of the visible value rows (all context rows and chunk rows 0..i)."""
+    H, G, n_c, n_in, d = 2, 3, 11, 6, 5
+    q = _rand((H, G, n_in, d), 81)
+    kc = _rand((H, n_c, d), 82)
+    ki = _rand((H, n_in, d), 83)
+    O = ras.chunk_attention_output(q, kc, ki, np.ones((H, n_c, 4)), np.ones((H, n_in, 4)), 0.6)
+    np.testing.assert_allclose(O, 1.0, rtol=0, atol=1e-14)
+    vc = _rand((H, n_c, d), 84)
+    vi = _rand((H, n_in, d), 85)
+    O0 = ras.chunk_attention_output(np.zeros_like(q), kc, ki, vc, vi, 0.6)
+    for h in range(H):
+        for i in range(n_in):
+            vis = np.concatenate([vc[h], vi[h, : i + 1]])
+            for g in range(G):
+                np.testing.assert_allclose(O0[h, g, i], vis.mean(axis=0), rtol=1e-13, atol=1e-15)
+
+
+def test_attention_output_single_row_is_library_attention():
+    """n_in = 1 (no prompt, one copied token): O is torch's scaled dot-product
+    attention of that query over [K_c; k_0] and [V_c; v_0] in fp64."""
+    torch = pytest.importorskip("torch")
+    H, G, n_c, d = 2, 2, 23, 8
+    q = _rand((H, G, 1, d), 86)
+    kc = _rand((H, n_c, d), 87)
+    ki = _rand((H, 1, d), 88)
+    vc = _rand((H, n_c, d), 89)
+    vi = _rand((H, 1, d), 90)
+    O = ras.chunk_attention_output(q, kc, ki, vc, vi, 0.3)
+    for h in range(H):
+        keys = torch.from_numpy(np.concatenate([kc[h], ki[h]]))[None]
+        vals = torch.from_numpy(np.concatenate([vc[h], vi[h]]))[None]
+        want = torch.nn.functional.scaled_dot_product_attention(
+            torch.from_numpy(q[h, :, 0])[None], keys, vals, scale=0.3)[0].numpy()
+        np.testing.assert_allclose(O[h, :, 0], want, rtol=1e-12, atol=1e-14)
+
+
+def test_attention_output_brute_force_pure_python():
+    """Tiny case by pure-Python loops (math.exp, math.fsum), causal key set;
+    value rows differ from key rows, so a P.K or transposed contraction fails."""
+    H, G, n_c, n_in, d, dv = 1, 2, 4, 3, 3, 2
+    q = _rand((H, G, n_in, d), 91)
+    kc = _rand((H, n_c, d), 92)
+    ki = _rand((H, n_in, d), 93)
+    vc = _rand((H, n_c, dv), 94)
+    vi = _rand((H, n_in, dv), 95)
+    scale = 0.8
+    O = ras.chunk_attention_output(q, kc, ki, vc, vi, scale)
+    for g in range(G):
+        for i in range(n_in):
+            keys = [kc[0, j] for j in range(n_c)] + [ki[0, t] for t in range(i + 1)]
+            vals = [vc[0, j] for j in range(n_c)] + [vi[0, t] for t in range(i + 1)]
+            lg = [scale * math.fsum(float(a) * float(b) for a, b in zip(q[0, g, i], k))
+                  for k in keys]
+            m = max(lg)
+            w = [math.exp(x - m) for x in lg]
+            z = math.fsum(w)
+            for c in range(dv):
+                want = math.fsum(wk * float(v[c]) for wk, v in zip(w, vals)) / z
+                assert abs(O[0, g, i, c] - want) <= 1e-13 * max(1.0, abs(want))
+
+
+def test_attention_output_one_hot_values_give_probabilities():
+    """Value row j = unit vector e_j: O equals the probability matrix, so the
+    output and the scores come from the same softmax rows."""
+    H, G, n_c, n_in, d = 1, 2, 7, 5, 6
+    q = _rand((H, G, n_in, d), 96, 2.0)
+    kc = _rand((H, n_c, d), 97)
+    ki = _rand((H, n_in, d), 98)
+    eye = np.eye(n_c + n_in)
+    O = ras.chunk_attention_output(q, kc, ki, eye[None, :n_c], eye[None, n_c:], 0.5)
+    for g in range(G):
+        P = ras.chunk_probabilities(q[0, g], kc[0], ki[0], 0.5)
+        np.testing.assert_allclose(O[0, g], P, rtol=0, atol=1e-15)
