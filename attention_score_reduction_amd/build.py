@@ -5,7 +5,8 @@ import sys
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
-SOURCES = ["api.hip", "score.hip", "select.hip", "compact.hip", "heads.hip", "decode.hip"]
+SOURCES = ["api.hip", "score.hip", "attn.hip", "select.hip", "compact.hip", "heads.hip",
+           "decode.hip"]
 LIB = os.path.join(HERE, "libkvz.so")
 
 FLAGS = [

@@ -112,6 +112,39 @@ kvz_status kvz_score_chunk(kvz_dtype dt, int H, int G, int d, int n_c, int n_pro
                             S, ws, ws_bytes, stream);
 }
 
+size_t kvz_score_chunk_attn_workspace(kvz_dtype dt, int H, int G, int n_in, int d, int n_c) {
+  if ((dt != KVZ_BF16 && dt != KVZ_F32) || !head_dim_ok(d) || H < 1 || G < 1 || n_in < 1 ||
+      n_c < 1 || (long long)G * n_in > (1 << 20) || n_c > (1 << 24))
+    return 0;
+  const ScorePlan p = score_plan(dt, H, G, n_in, d, n_c);
+  return p.total_bytes + attn_plan(dt, p).part_bytes;
+}
+
+kvz_status kvz_score_chunk_attn(kvz_dtype dt, int H, int G, int d, int n_c, int n_prompt,
+                                int n_in, const void* q, const void* k_ctx, const void* k_in,
+                                const void* v_ctx, const void* v_in, float scale, float* S,
+                                float* O, void* ws, size_t ws_bytes, void* stream) {
+  if (dt != KVZ_BF16 && dt != KVZ_F32) return KVZ_ERR_UNSUPPORTED;
+  if (!head_dim_ok(d)) return KVZ_ERR_UNSUPPORTED;
+  if (H < 1 || G < 1 || n_in < 1 || n_c < 1 || n_prompt < 0 || n_prompt > n_in)
+    return KVZ_ERR_INVALID_ARG;
+  if ((long long)G * n_in > (1 << 20) || n_c > (1 << 24)) return KVZ_ERR_INVALID_ARG;
+  if (!q || !k_ctx || !k_in || !v_ctx || !v_in || !S || !O || !ws) return KVZ_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(k_ctx) || !aligned16(k_in) || !aligned16(v_ctx) ||
+      !aligned16(v_in) || !aligned16(S) || !aligned16(O))
+    return KVZ_ERR_INVALID_ARG;
+  if ((reinterpret_cast<uintptr_t>(ws) & 255u) != 0) return KVZ_ERR_INVALID_ARG;
+  if (!(scale > 0.f) || !isfinite(scale)) return KVZ_ERR_INVALID_ARG;
+  const ScorePlan p = score_plan(dt, H, G, n_in, d, n_c);
+  const AttnPlan a = attn_plan(dt, p);
+  if (ws_bytes < p.total_bytes + a.part_bytes) return KVZ_ERR_WORKSPACE;
+  clear_error();
+  const hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  hipError_t e = score_launch(dt, KVZ_AGG_MAX, p, q, k_ctx, k_in, scale, S, ws, st);
+  if (e == hipSuccess) e = attn_launch(dt, p, a, q, k_ctx, k_in, v_ctx, v_in, scale, O, ws, st);
+  return e == hipSuccess ? KVZ_OK : KVZ_ERR_HIP;
+}
+
 kvz_status kvz_head_scores(const float* S, int64_t n_heads, int n_c, float* head_score,
                            void* stream) {
   if (n_heads < 1 || n_c < 1 || n_heads > (int64_t(1) << 31) - 1) return KVZ_ERR_INVALID_ARG;
@@ -255,7 +288,8 @@ kvz_status kvz_prof_read(const char* name, int64_t* launches, double* total_ms) 
                                  "select_pick",   "select_tile_count", "select_scan",
                                  "select_mask",   "compact_count",     "compact_scan",
                                  "compact_scatter", "head_scores",    "token_scores",
-                                 "decode_split",  "decode_combine"};
+                                 "decode_split",  "decode_combine",    "attn_pass3",
+                                 "attn_reduce"};
   for (const char* k : kNames) known |= strcmp(k, name) == 0;
   if (!known) return KVZ_ERR_INVALID_ARG;
   for (const ProfRec& r : p.recs) {

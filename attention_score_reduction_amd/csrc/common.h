@@ -87,6 +87,19 @@ hipError_t score_launch(kvz_dtype dt, kvz_aggregate agg, const ScorePlan& p, con
                         const void* kc, const void* kin, float scale, float* S, void* ws,
                         hipStream_t st);
 
+// reconstruction attention output (after the score passes of the same call,
+// reusing their row log-sum-exp from the score workspace)
+struct AttnPlan {
+  int n_rt;             // row tiles of 128 rows per head
+  int n_split_ctx;      // splits of the context keys (+1 in-chunk split)
+  int tiles_per_split;  // 32-key tiles per context split
+  size_t part_bytes;    // partial outputs, after the score workspace
+};
+AttnPlan attn_plan(kvz_dtype dt, const ScorePlan& p);
+hipError_t attn_launch(kvz_dtype dt, const ScorePlan& p, const AttnPlan& a, const void* q,
+                       const void* kc, const void* kin, const void* vc, const void* vin,
+                       float scale, float* O, void* ws, hipStream_t st);
+
 hipError_t head_scores_launch(const float* S, int64_t n_heads, int n_c, float* out,
                               hipStream_t st);
 hipError_t token_scores_launch(const float* S, int64_t n_heads, int n_c, float* out,

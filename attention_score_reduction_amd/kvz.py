@@ -21,6 +21,7 @@ AGG = {"max": KVZ_AGG_MAX, "sum": KVZ_AGG_SUM, "raw": KVZ_AGG_RAW_MAX}
 # every symbol declared in include/kvz.h
 SYMBOLS = (
     "kvz_status_string", "kvz_score_chunk_workspace", "kvz_score_chunk", "kvz_score_chunk_ex",
+    "kvz_score_chunk_attn_workspace", "kvz_score_chunk_attn",
     "kvz_keep_count", "kvz_select_workspace", "kvz_select_threshold", "kvz_compact_workspace",
     "kvz_compact", "kvz_head_scores", "kvz_token_scores", "kvz_decode_workspace",
     "kvz_decode_packed", "kvz_prof_enable", "kvz_prof_read",
@@ -57,6 +58,11 @@ def lib():
     L.kvz_score_chunk_ex.argtypes = [c_int, c_int, c_int, c_int, c_int, c_int, c_int, c_int, c_p,
                                      c_p, c_p, c_f, c_p, c_p, c_sz, c_p]
     L.kvz_score_chunk_ex.restype = c_int
+    L.kvz_score_chunk_attn_workspace.argtypes = [c_int, c_int, c_int, c_int, c_int, c_int]
+    L.kvz_score_chunk_attn_workspace.restype = c_sz
+    L.kvz_score_chunk_attn.argtypes = [c_int, c_int, c_int, c_int, c_int, c_int, c_int, c_p, c_p,
+                                       c_p, c_p, c_p, c_f, c_p, c_p, c_p, c_sz, c_p]
+    L.kvz_score_chunk_attn.restype = c_int
     L.kvz_head_scores.argtypes = [c_p, c_i64, c_int, c_p, c_p]
     L.kvz_head_scores.restype = c_int
     L.kvz_token_scores.argtypes = [c_p, c_i64, c_int, c_p, c_p]
@@ -168,6 +174,44 @@ def kvz_score_chunk_ex(q, k_ctx, k_in, S, n_prompt, agg="max", scale=None, ws=No
                                   _stream(stream))
     _check(st, "kvz_score_chunk_ex")
     return S
+
+
+def kvz_score_chunk_attn_workspace(dtype_code, H, G, n_in, d, n_c) -> int:
+    return int(lib().kvz_score_chunk_attn_workspace(dtype_code, H, G, n_in, d, n_c))
+
+
+def kvz_score_chunk_attn(q, k_ctx, k_in, v_ctx, v_in, S, n_prompt, O=None, scale=None, ws=None,
+                         stream=None):
+    """kvz_score_chunk plus the chunk's attention output O [H][G][n_in][d]
+    fp32 over the values v_ctx [H][n_c][d] and v_in [H][n_in][d].  Returns O."""
+    import torch
+    H, G, n_in, d = q.shape
+    n_c = k_ctx.shape[1]
+    if tuple(k_ctx.shape) != (H, n_c, d) or tuple(k_in.shape) != (H, n_in, d):
+        raise ValueError("shape mismatch between q, k_ctx and k_in")
+    if tuple(v_ctx.shape) != (H, n_c, d) or tuple(v_in.shape) != (H, n_in, d):
+        raise ValueError("shape mismatch between k and v")
+    if tuple(S.shape) != (H, n_c) or S.dtype != torch.float32:
+        raise ValueError("S must be fp32 [H][n_c]")
+    if any(t.dtype != q.dtype for t in (k_ctx, k_in, v_ctx, v_in)):
+        raise TypeError("q, k and v tensors must share a dtype")
+    dt = _dtype_code(q)
+    if O is None:
+        O = torch.empty(H, G, n_in, d, dtype=torch.float32, device=q.device)
+    if tuple(O.shape) != (H, G, n_in, d) or O.dtype != torch.float32:
+        raise ValueError("O must be fp32 [H][G][n_in][d]")
+    if scale is None:
+        scale = d ** -0.5
+    need = kvz_score_chunk_attn_workspace(dt, H, G, n_in, d, n_c)
+    if ws is None:
+        ws = _ws(need, q.device)
+    st = lib().kvz_score_chunk_attn(dt, H, G, d, n_c, int(n_prompt), n_in, _ptr(q, "q"),
+                                    _ptr(k_ctx, "k_ctx"), _ptr(k_in, "k_in"),
+                                    _ptr(v_ctx, "v_ctx"), _ptr(v_in, "v_in"), float(scale),
+                                    _ptr(S, "S"), _ptr(O, "O"), _ptr(ws, "ws"),
+                                    ws.numel() * ws.element_size(), _stream(stream))
+    _check(st, "kvz_score_chunk_attn")
+    return O
 
 
 def kvz_head_scores(S, out=None, stream=None):

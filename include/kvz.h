@@ -121,6 +121,34 @@ KVZ_API kvz_status kvz_score_chunk_ex(kvz_dtype dt, kvz_aggregate agg, int H, in
                                       void* ws, size_t ws_bytes, void* stream);
 
 /* ------------------------------------------------------------------------
+ * Scoring of one chunk together with the chunk's attention output: the
+ * fused reconstruction attention (rebuttal, computational analysis: the
+ * scoring stage is a full forward over [repeat prompt; chunk], one MLP pass
+ * and twice the prefill's attention work, so each layer's attention also
+ * feeds the layer above; blog 4.4: this product is what a FlashAttention
+ * kernel returns).
+ *
+ * Same S update, arguments, limits and errors as kvz_score_chunk, plus
+ *   v_ctx  [H][n_c][d]       the layer's cached context values (dtype dt),
+ *   v_in   [H][n_in][d]      values of the chunk's own tokens (dtype dt),
+ *   O      [H][G][n_in][d]   fp32, written (not accumulated):
+ *     O[h][g][i] = sum over the visible keys j of p[j] * v_j,
+ * with v_j the rows of [v_ctx[h]; v_in[h]] and p the softmax row of query
+ * (h, g, i) that the scores are taken from.  bf16 inputs: p is rounded to
+ * bf16 for the matrix product, sums in fp32.  All pointers device, 16-byte
+ * aligned; NULL or misaligned -> KVZ_ERR_INVALID_ARG.  Workspace:
+ * kvz_score_chunk_attn_workspace() bytes (it includes the score workspace),
+ * 256-byte aligned; too small -> KVZ_ERR_WORKSPACE.
+ * ---------------------------------------------------------------------- */
+KVZ_API size_t kvz_score_chunk_attn_workspace(kvz_dtype dt, int H, int G, int n_in, int d,
+                                              int n_c);
+KVZ_API kvz_status kvz_score_chunk_attn(kvz_dtype dt, int H, int G, int d, int n_c, int n_prompt,
+                                        int n_in, const void* q, const void* k_ctx,
+                                        const void* k_in, const void* v_ctx, const void* v_in,
+                                        float scale, float* S, float* O, void* ws,
+                                        size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
  * Head-level score (rebuttal, answer on head-level scores: the max of S along
  * the sequence axis, used for context-independent head eviction):
  *   head_score[h] = max over j of S[h][j]        (device fp32 [n_heads])

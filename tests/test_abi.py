@@ -84,6 +84,38 @@ def test_score_validation(kw, status):
     assert _score(**kw) == status
 
 
+def _attn(**kw):
+    a = dict(dt=0, H=2, G=4, d=128, n_c=100, n_prompt=4, n_in=20, q=FAKE, kc=FAKE, ki=FAKE,
+             vc=FAKE, vi=FAKE, scale=0.1, S=FAKE, O=FAKE, ws=FAKE, wsb=1 << 30, stream=None)
+    a.update(kw)
+    return kvz.lib().kvz_score_chunk_attn(a["dt"], a["H"], a["G"], a["d"], a["n_c"], a["n_prompt"],
+                                          a["n_in"], a["q"], a["kc"], a["ki"], a["vc"], a["vi"],
+                                          a["scale"], a["S"], a["O"], a["ws"], a["wsb"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(d=96), kvz.KVZ_ERR_UNSUPPORTED), (dict(dt=7), kvz.KVZ_ERR_UNSUPPORTED),
+    (dict(H=0), kvz.KVZ_ERR_INVALID_ARG), (dict(n_prompt=21), kvz.KVZ_ERR_INVALID_ARG),
+    (dict(vc=None), kvz.KVZ_ERR_INVALID_ARG), (dict(vi=None), kvz.KVZ_ERR_INVALID_ARG),
+    (dict(O=None), kvz.KVZ_ERR_INVALID_ARG), (dict(vi=MIS), kvz.KVZ_ERR_INVALID_ARG),
+    (dict(O=MIS), kvz.KVZ_ERR_INVALID_ARG), (dict(scale=0.0), kvz.KVZ_ERR_INVALID_ARG),
+    (dict(wsb=16), kvz.KVZ_ERR_WORKSPACE),
+])
+def test_score_attn_validation(kw, status):
+    assert _attn(**kw) == status
+
+
+def test_score_attn_workspace_covers_score_workspace():
+    for dt, d in ((kvz.KVZ_BF16, 128), (kvz.KVZ_BF16, 256), (kvz.KVZ_F32, 64)):
+        a = kvz.kvz_score_chunk_attn_workspace(dt, 8, 4, 2064, d, 131072)
+        s = kvz.kvz_score_chunk_workspace(dt, 8, 4, 2064, d, 131072)
+        assert a >= s > 0
+    assert kvz.kvz_score_chunk_attn_workspace(kvz.KVZ_BF16, 8, 4, 2064, 96, 131072) == 0
+    # exactly the required size passes validation, one byte less does not
+    need = kvz.kvz_score_chunk_attn_workspace(kvz.KVZ_BF16, 2, 4, 20, 128, 100)
+    assert _attn(wsb=need - 1) == kvz.KVZ_ERR_WORKSPACE
+
+
 def test_score_ex_rejects_unknown_aggregation():
     L = kvz.lib()
     r = L.kvz_score_chunk_ex(0, 7, 2, 4, 128, 100, 4, 20, FAKE, FAKE, FAKE, 0.1, FAKE, FAKE,

@@ -1,0 +1,178 @@
+"""Parity of the fused reconstruction attention (scores plus the chunk's
+attention output O = P [V_c; V_in]) with the fp64 oracle.
+
+Tolerances: scores as for kvz_score_chunk.  O for bf16 inputs: the
+probabilities are rounded to bf16 (relative 2^-9) before the product with the
+exact bf16 values and summed in fp32, so |dO| <= 2^-9 sum_j p_j |v_j|; held to
+2e-3 + 1e-2 |O|.  O for fp32 inputs: 1e-5 + 1e-4 |O|.
+"""
+import math
+
+import numpy as np
+import pytest
+
+from attention_score_reduction_amd import kvz
+from attention_score_reduction_amd.inputs import WORKLOADS, HostGen, Workload, bf16_bits
+from oracle import ras
+from tests.helpers import assert_scores_close, to_dev
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+O_ATOL, O_RTOL = 2e-3, 1e-2
+
+
+def run_chunks(gen, layer, chunk_ids, heads=None):
+    """GPU scores of the listed chunks and the output O of each chunk."""
+    wl = gen.wl
+    kc, vc = gen.context(layer, heads)
+    kc_d, vc_d = to_dev(kc, wl.dtype), to_dev(vc, wl.dtype)
+    S = torch.zeros(kc.shape[0], wl.n_ctx, dtype=torch.float32, device="cuda")
+    outs = []
+    for k in chunk_ids:
+        q, kin = gen.chunk_inputs(layer, k, heads)
+        vin = gen.chunk_values(layer, k, heads)
+        O = kvz.kvz_score_chunk_attn(to_dev(q, wl.dtype), kc_d, to_dev(kin, wl.dtype), vc_d,
+                                     to_dev(vin, wl.dtype), S, wl.n_prompt,
+                                     scale=1.0 / math.sqrt(wl.head_dim))
+        outs.append(O)
+    torch.cuda.synchronize()
+    return S.cpu().numpy(), [o.cpu().numpy() for o in outs]
+
+
+def oracle_chunks(gen, layer, chunk_ids, heads):
+    wl = gen.wl
+    kc, vc = gen.context(layer, heads)
+    kc64, vc64 = ras.to_f64(kc, wl.dtype), ras.to_f64(vc, wl.dtype)
+    scale = 1.0 / math.sqrt(wl.head_dim)
+    S = np.zeros((len(heads), wl.n_ctx))
+    outs = []
+    for k in chunk_ids:
+        q, kin = gen.chunk_inputs(layer, k, heads)
+        vin = gen.chunk_values(layer, k, heads)
+        q64, k64, v64 = (ras.to_f64(x, wl.dtype) for x in (q, kin, vin))
+        ras.score_chunk(q64, kc64, k64, scale, S)
+        outs.append(ras.chunk_attention_output(q64, kc64, k64, vc64, v64, scale))
+    return S, outs
+
+
+def test_tiny_fp32_workload_full():
+    gen = HostGen(WORKLOADS["tiny_fp32"])
+    S, O = run_chunks(gen, 0, [0])
+    Sr, Or = oracle_chunks(gen, 0, [0], [0])
+    assert_scores_close(S, Sr, atol=1e-6, rtol=1e-4, what="tiny fp32 S")
+    assert_scores_close(O[0], Or[0], atol=1e-5, rtol=1e-4, what="tiny fp32 O")
+
+
+SMALL = [
+    # (name, H, G, d, n_c, chunk, n_prompt, sigma, sink)
+    ("d128_g4_ragged", 2, 4, 128, 1000, 300, 16, 0.5, True),
+    ("d64_g5", 2, 5, 64, 777, 250, 16, 0.0, False),
+    ("d256_g2", 1, 2, 256, 1500, 640, 16, 1.0, False),
+    ("d128_g1_one_row_tail", 1, 1, 128, 513, 512, 7, 0.3, True),
+]
+
+
+@pytest.mark.parametrize("case", SMALL, ids=[c[0] for c in SMALL])
+def test_small_bf16_shapes(case):
+    """Several tiles, ragged context tail, causal chunk keys, G not a power
+    of two, every chunk (the last one ragged)."""
+    name, H, G, d, n_c, chunk, n_p, sig, sink = case
+    wl = Workload(name, 21, 1, H, G, d, n_c, chunk, n_p, 0.3, key_lognormal_sigma=sig, sink=sink)
+    gen = HostGen(wl)
+    ids = list(range(len(wl.chunks())))
+    S, O = run_chunks(gen, 0, ids)
+    Sr, Or = oracle_chunks(gen, 0, ids, list(range(H)))
+    assert_scores_close(S, Sr, what=f"{name} S")
+    for k in ids:
+        assert_scores_close(O[k], Or[k], atol=O_ATOL, rtol=O_RTOL, what=f"{name} O chunk {k}")
+
+
+def test_scores_equal_kvz_score_chunk_bitwise():
+    """The fused call's score update is the plain score call's, bit for bit."""
+    wl = Workload("same", 22, 1, 2, 4, 128, 1100, 400, 16, 0.3, key_lognormal_sigma=0.5, sink=True)
+    gen = HostGen(wl)
+    S, _ = run_chunks(gen, 0, [0, 1, 2])
+    kc, _ = gen.context(0)
+    kc_d = to_dev(kc, "bf16")
+    S2 = torch.zeros(2, wl.n_ctx, dtype=torch.float32, device="cuda")
+    for k in (0, 1, 2):
+        q, kin = gen.chunk_inputs(0, k)
+        kvz.kvz_score_chunk(to_dev(q, "bf16"), kc_d, to_dev(kin, "bf16"), S2, wl.n_prompt,
+                            1 / math.sqrt(128))
+    assert np.array_equal(S, S2.cpu().numpy())
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_closed_forms(dtype):
+    """Q = 0: every visible key gets the same weight, so O_i is the mean of
+    the visible value rows (context rows and chunk rows 0..i).  V = 1: O = 1."""
+    H, G, d, n_c, n_in = 2, 3, 64 if dtype == "f32" else 128, 900, 150
+    rng = np.random.default_rng(23)
+    kc = rng.standard_normal((H, n_c, d)).astype(np.float32)
+    ki = rng.standard_normal((H, n_in, d)).astype(np.float32)
+    vc = rng.standard_normal((H, n_c, d)).astype(np.float32)
+    vi = rng.standard_normal((H, n_in, d)).astype(np.float32)
+    q = np.zeros((H, G, n_in, d), np.float32)
+    conv = bf16_bits if dtype == "bf16" else (lambda x: x)
+    kc, ki, vc, vi, q = (conv(x) for x in (kc, ki, vc, vi, q))
+    S = torch.zeros(H, n_c, dtype=torch.float32, device="cuda")
+    O = kvz.kvz_score_chunk_attn(to_dev(q, dtype), to_dev(kc, dtype), to_dev(ki, dtype),
+                                 to_dev(vc, dtype), to_dev(vi, dtype), S, 8).cpu().numpy()
+    vc64, vi64 = ras.to_f64(vc, dtype), ras.to_f64(vi, dtype)
+    want = np.zeros_like(O, dtype=np.float64)
+    for h in range(H):
+        csum = vc64[h].sum(axis=0)
+        run = np.cumsum(vi64[h], axis=0)
+        for i in range(n_in):
+            want[h, :, i] = (csum + run[i]) / (n_c + i + 1)
+    tol = (O_ATOL, O_RTOL) if dtype == "bf16" else (1e-5, 1e-4)
+    assert_scores_close(O, want, atol=tol[0], rtol=tol[1], what=f"Q=0 O {dtype}")
+    ones = conv(np.ones((H, n_c, d), np.float32))
+    ones_in = conv(np.ones((H, n_in, d), np.float32))
+    q2 = conv(rng.standard_normal((H, G, n_in, d)).astype(np.float32))
+    O1 = kvz.kvz_score_chunk_attn(to_dev(q2, dtype), to_dev(kc, dtype), to_dev(ki, dtype),
+                                  to_dev(ones, dtype), to_dev(ones_in, dtype), S, 8).cpu().numpy()
+    np.testing.assert_allclose(O1, 1.0, atol=2e-3 if dtype == "bf16" else 1e-5, rtol=0)
+
+
+def test_llama8b_8k_layer_sampled_heads():
+    """8192-token LLaMA3.1-8B-shaped layer: all heads on the GPU, first and
+    last chunk, two heads in the oracle."""
+    wl = WORKLOADS["llama8b_8k"]
+    gen = HostGen(wl)
+    ids = [0, 3]
+    S, O = run_chunks(gen, 2, ids)
+    heads = [1, 6]
+    Sr, Or = oracle_chunks(gen, 2, ids, heads)
+    assert_scores_close(S[heads], Sr, what="llama8b_8k S")
+    for n, k in enumerate(ids):
+        assert_scores_close(O[n][heads], Or[n], atol=O_ATOL, rtol=O_RTOL, what=f"llama8b_8k O {k}")
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("name", ["llama8b_128k", "gemma12b_170k"])
+def test_full_size_chunk_sampled_rows(name):
+    """Full-size layer in one call (all heads, the benchmark's launch shape);
+    sampled rows of two heads through the oracle, one dense softmax row at a
+    time (prompt rows, first and last copied rows, random rows)."""
+    wl = WORKLOADS[name]
+    gen = HostGen(wl)
+    _, O = run_chunks(gen, 0, [0])
+    kc, vc = gen.context(0)
+    q, kin = gen.chunk_inputs(0, 0)
+    vin = gen.chunk_values(0, 0)
+    n_in = wl.n_in(0)
+    scale = 1 / math.sqrt(wl.head_dim)
+    rng = np.random.default_rng(24)
+    rows = sorted(set([0, wl.n_prompt - 1, wl.n_prompt, n_in - 1] +
+                      rng.choice(n_in, 12, replace=False).tolist()))
+    for h in (0, wl.heads - 1):
+        kc64, vc64 = ras.to_f64(kc[h], wl.dtype), ras.to_f64(vc[h], wl.dtype)
+        ki64, vi64 = ras.to_f64(kin[h], wl.dtype), ras.to_f64(vin[h], wl.dtype)
+        vals = np.concatenate([vc64, vi64])
+        for g in (0, wl.group - 1):
+            P = ras.chunk_probabilities(ras.to_f64(q[h, g], wl.dtype), kc64, ki64, scale, rows)
+            assert_scores_close(O[0][h, g, rows], P @ vals, atol=O_ATOL, rtol=O_RTOL,
+                                what=f"{name} O h{h} g{g}")
