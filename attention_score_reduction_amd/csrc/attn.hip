@@ -63,9 +63,9 @@ __global__ __launch_bounds__(256) void attn_pass3_bf16(
   constexpr int KS = G3<D>::KS, CH = G3<D>::CH, SWZ = G3<D>::SWZ, DT = G3<D>::DT;
   constexpr int VSTR = G3<D>::VSTR;
   constexpr int LOADS = KT * CH / 256;
-  __shared__ uint4 ldk[KT * CH];
-  __shared__ uint4 ldv4[D * VSTR / 8];
-  uint16_t* ldv = reinterpret_cast<uint16_t*>(ldv4);
+  // two LDS stages of K (row-major, swizzled) and V^T
+  __shared__ uint4 ldk[2][KT * CH];
+  __shared__ uint4 ldv4[2][D * VSTR / 8];
 
   const int lb = xcd_logical_block();
   if (lb >= n_blocks) return;
@@ -114,35 +114,45 @@ __global__ __launch_bounds__(256) void attn_pass3_bf16(
 #pragma unroll
   for (int t = 0; t < DT; ++t) o[t] = f32x16{};
 
+  // K copies: chunk-fastest (16-byte rows of one key per 16 lanes); V copies:
+  // key-fastest, so the transposed 2-byte LDS writes of a wave land in
+  // consecutive slots of one V^T row
   uint4 kreg[LOADS], vreg[LOADS];
   auto load = [&](int tile) {
 #pragma unroll
     for (int u = 0; u < LOADS; ++u) {
-      const int c = tid + 256 * u, row = c / CH, ch = c % CH, key = tile * KT + row;
-      const bool ok = key < nkeys;
-      kreg[u] = ok ? ld16(kbase + (size_t)key * D + ch * 8) : make_uint4(0, 0, 0, 0);
-      vreg[u] = ok ? ld16(vbase + (size_t)key * D + ch * 8) : make_uint4(0, 0, 0, 0);
+      const int c = tid + 256 * u;
+      const int krow = c / CH, kch = c % CH, key = tile * KT + krow;
+      kreg[u] = key < nkeys ? ld16(kbase + (size_t)key * D + kch * 8) : make_uint4(0, 0, 0, 0);
+      const int vrow = c % KT, vch = c / KT, vkey = tile * KT + vrow;
+      vreg[u] = vkey < nkeys ? ld16(vbase + (size_t)vkey * D + vch * 8) : make_uint4(0, 0, 0, 0);
     }
   };
-  auto store = [&]() {
+  auto store = [&](int buf) {
+    uint16_t* ldv = reinterpret_cast<uint16_t*>(ldv4[buf]);
 #pragma unroll
     for (int u = 0; u < LOADS; ++u) {
-      const int c = tid + 256 * u, row = c / CH, ch = c % CH;
-      ldk[row * CH + (ch ^ (row & SWZ))] = kreg[u];
-      const int sl = vslot(row);
+      const int c = tid + 256 * u;
+      const int krow = c / CH, kch = c % CH;
+      ldk[buf][krow * CH + (kch ^ (krow & SWZ))] = kreg[u];
+      const int vrow = c % KT, vch = c / KT;
+      const int sl = vslot(vrow);
       const uint32_t w[4] = {vreg[u].x, vreg[u].y, vreg[u].z, vreg[u].w};
 #pragma unroll
       for (int e = 0; e < 8; ++e)
-        ldv[(ch * 8 + e) * VSTR + sl] = (uint16_t)(w[e >> 1] >> (16 * (e & 1)));
+        ldv[(vch * 8 + e) * VSTR + sl] = (uint16_t)(w[e >> 1] >> (16 * (e & 1)));
     }
   };
 
-  if (t_begin < t_end) load(t_begin);
+  if (t_begin < t_end) {
+    load(t_begin);
+    store(0);
+  }
+  __syncthreads();
   for (int tile = t_begin; tile < t_end; ++tile) {
-    __syncthreads();
-    store();
-    __syncthreads();
-    if (tile + 1 < t_end) load(tile + 1);
+    const int buf = (tile - t_begin) & 1;
+    const bool more = tile + 1 < t_end;
+    if (more) load(tile + 1);
     // logits of the lane's query column over the tile's 32 keys, offset by
     // the row's -lse2/(scale log2 e)
     f32x16 c;
@@ -150,16 +160,21 @@ __global__ __launch_bounds__(256) void attn_pass3_bf16(
     for (int v = 0; v < 16; ++v) c[v] = start;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-      const bf16x8 a = as_bf16x8(ldk[n * CH + ((ks * 2 + half) ^ (n & SWZ))]);
+      const bf16x8 a = as_bf16x8(ldk[buf][n * CH + ((ks * 2 + half) ^ (n & SWZ))]);
       c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qr[ks], c, 0, 0, 0);
     }
     const int key0 = tile * KT;
     float p[16];
+    if (!inchunk && key0 + KT <= n_c) {
 #pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      const int key = key0 + acc_row3(v, half);
-      const bool vis = inchunk ? key <= irow : key < n_c;
-      p[v] = vis ? fast_exp2(c[v] * cl2) : 0.f;
+      for (int v = 0; v < 16; ++v) p[v] = fast_exp2(c[v] * cl2);
+    } else {
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int key = key0 + acc_row3(v, half);
+        const bool vis = inchunk ? key <= irow : key < n_c;
+        p[v] = vis ? fast_exp2(c[v] * cl2) : 0.f;
+      }
     }
     bf16x8 pb[2];
 #pragma unroll
@@ -167,6 +182,7 @@ __global__ __launch_bounds__(256) void attn_pass3_bf16(
 #pragma unroll
       for (int i = 0; i < 8; ++i) pb[qq][i] = (__bf16)p[8 * qq + i];
     // O^T[d][query] += V^T[d][key] P[key][query]
+    const uint16_t* ldv = reinterpret_cast<const uint16_t*>(ldv4[buf]);
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) {
 #pragma unroll
@@ -176,6 +192,9 @@ __global__ __launch_bounds__(256) void attn_pass3_bf16(
         o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[qq], o[dt], 0, 0, 0);
       }
     }
+    // the other stage was last read one tile ago, before the last barrier
+    if (more) store(buf ^ 1);
+    __syncthreads();
   }
 
   // lane (n, half) holds d = 32 dt + 8 vg + 4 half + 0..3 of query row r

@@ -108,6 +108,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true",
                     help="skip the decode-attention comparison after the timed steps")
+    ap.add_argument("--no-attn", action="store_true",
+                    help="skip the fused attention-output measurement after the timed steps")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="after the timed steps, run a 2 GiB device-to-device copy (a plain copy "
                          "kernel of known size, to scale the HBM traffic counters)")
@@ -310,6 +312,50 @@ def main():
             "what": f"one decode token for all {G * n_heads} query heads over all {n_heads} "
                     "(layer, KV head) caches",
         }
+    # fused reconstruction attention (scores plus the chunk's output
+    # O = P [V_c; V_in]) on the first chunk of layer 0, outside the headline
+    # step: per-kernel times of one call and the output pass's MFMA rate
+    if not args.no_attn:
+        import torch as _t
+        k0 = 0
+        n_in0 = wl.n_prompt + chunks[k0][1]
+        gv = _t.Generator(device="cuda")
+        gv.manual_seed(wl.seed + 200)
+        v_in = _t.randn(H, n_in0, d, generator=gv, device=dev).to(tdt)
+        o_buf = _t.empty(H, G, n_in0, d, dtype=_t.float32, device=dev)
+        ws_attn = _t.empty(kvz.kvz_score_chunk_attn_workspace(dt_code, H, G, n_in0, d, n_c),
+                           dtype=_t.uint8, device=dev)
+        S_attn = _t.zeros(H, n_c, dtype=_t.float32, device=dev)
+
+        def attn_call():
+            kvz.kvz_score_chunk_attn(data["q"][0][k0], data["kc"][0], data["kin"][0][k0],
+                                     data["vc"][0], v_in, S_attn, wl.n_prompt, O=o_buf,
+                                     scale=scale, ws=ws_attn, stream=stream)
+
+        attn_call()
+        _t.cuda.synchronize()
+        reps = 5
+        kvz.kvz_prof_enable(True, 16 * reps)
+        for _ in range(reps):
+            attn_call()
+        _t.cuda.synchronize()
+        at = {}
+        for nm in ("score_pass1", "score_combine", "score_pass2", "attn_pass3", "attn_reduce"):
+            n_, ms_ = kvz.kvz_prof_read(nm)
+            if n_:
+                at[nm] = round(ms_ / n_ * 1e3, 2)
+        kvz.kvz_prof_enable(False)
+        # the output pass forms q.k once more and p.v once per visible (row, key) pair
+        vis = H * G * (n_in0 * n_c + n_in0 * (n_in0 + 1) // 2)
+        o_flops = 2 * d * vis * 2
+        if "attn_pass3" in at:
+            ach = o_flops / (at["attn_pass3"] * 1e-6) / 1e12
+            out["attn_output"] = {
+                "per_call_us": at, "call_us": round(sum(at.values()), 2),
+                "pass3_flops": o_flops, "pass3_TFLOPs": round(ach, 2),
+                "pass3_frac": round(ach / MFMA_BF16_PEAK_TFLOPS, 4),
+                "what": "kvz_score_chunk_attn on one 16+2048-row chunk of one layer "
+                        "(all KV heads): scores plus O = P[V_c; V_in]"}
     if args.copy_calibration:
         nbytes = 2 << 30
         src_t = torch.ones(nbytes // 4, dtype=torch.float32, device=dev)
