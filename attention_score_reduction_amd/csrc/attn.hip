@@ -16,9 +16,10 @@
 // pass 1); per 32-key tile one wave computes its 32 rows' logits on MFMA with
 // the accumulator started at the row's -lse2/(scale log2 e), so
 // p = 2^(scale log2 e * acc); p is rounded to bf16 and, still in the
-// accumulator layout, is the B operand of O^T += V^T P.  V tiles are stored
-// transposed in LDS (keys contiguous per d index) in the key order that
-// layout implies.  fp32 path: a plain VALU kernel for small fp32 problems.
+// accumulator layout, is the B operand of O^T += V^T P.  V tiles stay
+// row-major in LDS; the A operand (keys contiguous per d index, in the key
+// order that layout implies) comes from transposing LDS reads.  fp32 path: a
+// plain VALU kernel for small fp32 problems.
 #include "common.h"
 
 namespace kvz {
@@ -35,24 +36,40 @@ constexpr int ROWS3 = 128;  // query rows per workgroup (4 waves x 32)
 template <int D>
 struct G3 {
   static constexpr int KS = D / 16, CH = D / 8, SWZ = (CH < 16 ? CH : 16) - 1, DT = D / 32;
-  static constexpr int VSTR = 40;  // V^T row stride in bf16: 32 keys + 8 pad (80 B)
+  static constexpr int NB = D / 16;                  // 32-byte blocks per V row
+  static constexpr int VSW = (NB < 8 ? NB : 8) - 1;  // V block swizzle mask
 };
-
-// LDS slot of key kk (0..31) in a V^T row.  MFMA q (keys 16q..16q+15) takes
-// k-slot s of lane half h as the key held by accumulator v = 8q + (s & 7) of
-// that half: 16q + 8((s&7) >> 2) + 4h + (s & 3); this is its inverse.
-__device__ __forceinline__ int vslot(int kk) {
-  const int q = kk >> 4, kl = kk & 15;
-  return q * 16 + ((kl >> 2) & 1) * 8 + 4 * (kl >> 3) + (kl & 3);
-}
 
 __device__ __forceinline__ int acc_row3(int v, int half) {
   return 8 * (v >> 2) + 4 * half + (v & 3);
 }
 
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+
+// 4 x 16-bit transposed LDS read: within each group of 16 lanes, lane 4a+b
+// receives element b of the 8-byte chunks addressed by lanes a, a+4, a+8
+// and a+12 of its group.
+__device__ __forceinline__ v4i16 lds_read_tr4(const void* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) v4i16*)(const_cast<void*>(p)));
+}
+
 // grid: H x splits x row tiles (XCD-remapped, head-major); rows i-major
 // (r = i*G + g).  nlse: [H][R_pad] g-major, -lse2/(scale log2 e) (padding
 // rows -inf).  opart: [splits][H][R_pad][D] fp32, rows i-major.
+//
+// K and V tiles (32 keys each) go global -> LDS by buffer loads with an LDS
+// destination, row-major: K with 16-byte chunks XOR-swizzled by the key
+// (conflict-free A-operand reads, as in score pass 1), V with 32-byte blocks
+// XOR-swizzled by the key.  The A operand of O^T += V^T P (lane m: d index,
+// eight keys) is read with transposing LDS reads: in a 16-lane group, lane
+// j = a + 4c points at 4 d values (4a..4a+3 past the group's d base) of the
+// group's key c, so lane 4a+b receives d = 4a+b of keys c = 0..3.  The keys
+// follow the order the P accumulator layout gives the MFMA's k index (lane
+// half h holds keys 8(v>>2) + 4h + (v&3)): k-slots 0..3 of half h are keys
+// 4h + 0..3, slots 4..7 keys 8 + 4h + 0..3 (plus 16 for the second MFMA of
+// the tile).  The block swizzle puts a group's four keys in four different
+// 32-byte blocks of the bank space.
 template <int D>
 __global__ __launch_bounds__(256) void attn_pass3_bf16(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ kc,
@@ -61,11 +78,11 @@ __global__ __launch_bounds__(256) void attn_pass3_bf16(
     int H, int G, int n_c, int n_in, int R, int R_pad, int n_rt, int n_split_ctx,
     int tiles_per_split, float cl2, int n_blocks) {
   constexpr int KS = G3<D>::KS, CH = G3<D>::CH, SWZ = G3<D>::SWZ, DT = G3<D>::DT;
-  constexpr int VSTR = G3<D>::VSTR;
+  constexpr int VSW = G3<D>::VSW;
   constexpr int LOADS = KT * CH / 256;
-  // two LDS stages of K (row-major, swizzled) and V^T
-  __shared__ uint4 ldk[2][KT * CH];
-  __shared__ uint4 ldv4[2][D * VSTR / 8];
+  // two stages, as separate objects so that a copy into one stage is never
+  // taken to alias the reads of the other
+  __shared__ uint4 ldk0[KT * CH], ldk1[KT * CH], ldv0[KT * CH], ldv1[KT * CH];
 
   const int lb = xcd_logical_block();
   if (lb >= n_blocks) return;
@@ -114,55 +131,50 @@ __global__ __launch_bounds__(256) void attn_pass3_bf16(
 #pragma unroll
   for (int t = 0; t < DT; ++t) o[t] = f32x16{};
 
-  // K copies: chunk-fastest (16-byte rows of one key per 16 lanes); V copies:
-  // key-fastest, so the transposed 2-byte LDS writes of a wave land in
-  // consecutive slots of one V^T row
-  uint4 kreg[LOADS], vreg[LOADS];
-  auto load = [&](int tile) {
+  // copies: slot p of a stage holds key p / CH; for K its 16-byte chunk
+  // (p % CH) ^ (key & SWZ), for V its 32-byte block ((p % CH) / 2) ^ (key & VSW)
+  const int seg_bytes = nkeys * D * 2;
+  int koff[LOADS], voff[LOADS];
 #pragma unroll
-    for (int u = 0; u < LOADS; ++u) {
-      const int c = tid + 256 * u;
-      const int krow = c / CH, kch = c % CH, key = tile * KT + krow;
-      kreg[u] = key < nkeys ? ld16(kbase + (size_t)key * D + kch * 8) : make_uint4(0, 0, 0, 0);
-      const int vrow = c % KT, vch = c / KT, vkey = tile * KT + vrow;
-      vreg[u] = vkey < nkeys ? ld16(vbase + (size_t)vkey * D + vch * 8) : make_uint4(0, 0, 0, 0);
-    }
-  };
-  auto store = [&](int buf) {
-    uint16_t* ldv = reinterpret_cast<uint16_t*>(ldv4[buf]);
-#pragma unroll
-    for (int u = 0; u < LOADS; ++u) {
-      const int c = tid + 256 * u;
-      const int krow = c / CH, kch = c % CH;
-      ldk[buf][krow * CH + (kch ^ (krow & SWZ))] = kreg[u];
-      const int vrow = c % KT, vch = c / KT;
-      const int sl = vslot(vrow);
-      const uint32_t w[4] = {vreg[u].x, vreg[u].y, vreg[u].z, vreg[u].w};
-#pragma unroll
-      for (int e = 0; e < 8; ++e)
-        ldv[(vch * 8 + e) * VSTR + sl] = (uint16_t)(w[e >> 1] >> (16 * (e & 1)));
-    }
-  };
-
-  if (t_begin < t_end) {
-    load(t_begin);
-    store(0);
+  for (int u = 0; u < LOADS; ++u) {
+    const int slot = (u * 4 + wave) * 64 + lane;
+    const int row = slot / CH, cp = slot % CH;
+    koff[u] = row * D * 2 + (cp ^ (row & SWZ)) * 16;
+    voff[u] = row * D * 2 + ((((cp >> 1) ^ (row & VSW)) << 1) | (cp & 1)) * 16;
   }
-  __syncthreads();
-  for (int tile = t_begin; tile < t_end; ++tile) {
-    const int buf = (tile - t_begin) & 1;
+  auto copy_tile = [&](int tile, int par) {
+    uint4* dk = par ? ldk1 : ldk0;
+    uint4* dv = par ? ldv1 : ldv0;
+#pragma unroll
+    for (int u = 0; u < LOADS; ++u) {
+      copy16_to_lds(kbase, seg_bytes, koff[u] + tile * (KT * D * 2), dk + (u * 4 + wave) * 64);
+      copy16_to_lds(vbase, seg_bytes, voff[u] + tile * (KT * D * 2), dv + (u * 4 + wave) * 64);
+    }
+  };
+  // transposed-read byte offsets of this lane within a V stage, per d tile:
+  // key 4*half + c (c = (lane & 15) >> 2), d = 32 dt + 16 mh + 4a
+  const int tr_c = (lane & 15) >> 2, tr_a = lane & 3, tr_mh = (lane >> 4) & 1;
+  const int tr_key = 4 * half + tr_c;
+  int vrd[DT];
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt)
+    vrd[dt] = tr_key * D * 2 + (((2 * dt + tr_mh) ^ (tr_key & VSW)) * 32) + tr_a * 8;
+
+  auto body = [&](int tile, int par) {
+    const uint4* sk = par ? ldk1 : ldk0;
+    const char* sv = reinterpret_cast<const char*>(par ? ldv1 : ldv0);
+    bf16x8 a[KS];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) a[ks] = as_bf16x8(sk[n * CH + ((ks * 2 + half) ^ (n & SWZ))]);
     const bool more = tile + 1 < t_end;
-    if (more) load(tile + 1);
+    if (more) copy_tile(tile + 1, par ^ 1);
     // logits of the lane's query column over the tile's 32 keys, offset by
     // the row's -lse2/(scale log2 e)
     f32x16 c;
 #pragma unroll
     for (int v = 0; v < 16; ++v) c[v] = start;
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      const bf16x8 a = as_bf16x8(ldk[buf][n * CH + ((ks * 2 + half) ^ (n & SWZ))]);
-      c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qr[ks], c, 0, 0, 0);
-    }
+    for (int ks = 0; ks < KS; ++ks) c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[ks], qr[ks], c, 0, 0, 0);
     const int key0 = tile * KT;
     float p[16];
     if (!inchunk && key0 + KT <= n_c) {
@@ -182,20 +194,32 @@ __global__ __launch_bounds__(256) void attn_pass3_bf16(
 #pragma unroll
       for (int i = 0; i < 8; ++i) pb[qq][i] = (__bf16)p[8 * qq + i];
     // O^T[d][query] += V^T[d][key] P[key][query]
-    const uint16_t* ldv = reinterpret_cast<const uint16_t*>(ldv4[buf]);
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) {
 #pragma unroll
       for (int qq = 0; qq < 2; ++qq) {
-        const bf16x8 a = as_bf16x8(
-            *reinterpret_cast<const uint4*>(ldv + (dt * 32 + n) * VSTR + qq * 16 + half * 8));
-        o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[qq], o[dt], 0, 0, 0);
+        const v4i16 lo = lds_read_tr4(sv + vrd[dt] + (16 * qq) * D * 2);
+        const v4i16 hi = lds_read_tr4(sv + vrd[dt] + (16 * qq + 8) * D * 2);
+        const v4i16 both[2] = {lo, hi};
+        o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, both), pb[qq],
+                                                        o[dt], 0, 0, 0);
       }
     }
-    // the other stage was last read one tile ago, before the last barrier
-    if (more) store(buf ^ 1);
+    __builtin_amdgcn_s_waitcnt(0);  // this wave's copies of the next tile have landed
     __syncthreads();
+  };
+
+  if (t_begin < t_end) {
+    copy_tile(t_begin, 0);
+    __builtin_amdgcn_s_waitcnt(0);
   }
+  __syncthreads();
+  int tile = t_begin;
+  for (; tile + 1 < t_end; tile += 2) {
+    body(tile, 0);
+    body(tile + 1, 1);
+  }
+  if (tile < t_end) body(tile, 0);
 
   // lane (n, half) holds d = 32 dt + 8 vg + 4 half + 0..3 of query row r
   float* op = opart + (((size_t)s * H + h) * R_pad + r) * D;
