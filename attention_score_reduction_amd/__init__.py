@@ -2,7 +2,8 @@
 MI355X (gfx950): a C-ABI HIP library (libkvz.so, include/kvz.h) and its
 Python binding (kvz.py)."""
 from .kvz import (KvzError, kvz_compact, kvz_compact_workspace, kvz_decode_packed,  # noqa: F401
-                  kvz_decode_workspace, kvz_head_scores,
-                  kvz_keep_count, kvz_prof_enable, kvz_prof_read, kvz_score_chunk,
-                  kvz_score_chunk_ex, kvz_score_chunk_workspace, kvz_select_threshold,
-                  kvz_select_workspace, kvz_status_string, kvz_token_scores)
+                  kvz_decode_workspace, kvz_head_scores, kvz_keep_count, kvz_prof_enable,
+                  kvz_prof_read, kvz_score_chunk, kvz_score_chunk_attn,
+                  kvz_score_chunk_attn_workspace, kvz_score_chunk_ex, kvz_score_chunk_workspace,
+                  kvz_select_threshold, kvz_select_workspace, kvz_status_string,
+                  kvz_token_scores)

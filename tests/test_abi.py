@@ -183,3 +183,11 @@ def test_prof_read_rejects_unknown_name():
     assert kvz.lib().kvz_prof_read(b"nope", ctypes.byref(n), ctypes.byref(ms)) == kvz.KVZ_ERR_INVALID_ARG
     assert kvz.lib().kvz_prof_read(b"score_pass1", ctypes.byref(n), ctypes.byref(ms)) == kvz.KVZ_OK
     assert n.value == 0
+
+
+def test_package_exports_every_binding():
+    """Every C entry point with a Python wrapper is reachable from the package."""
+    import attention_score_reduction_amd as pkg
+    for n in kvz.SYMBOLS:
+        if hasattr(kvz, n):
+            assert hasattr(pkg, n), n
