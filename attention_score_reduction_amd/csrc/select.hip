@@ -41,6 +41,7 @@ constexpr int JBINS = 1 << 21;    // joint histogram of bits 20..0
 constexpr int TILE = 4096;        // scores per mask tile (within one head)
 constexpr int TPB = 256;          // threads per block
 constexpr int PER_T = TILE / TPB; // 16 scores per thread per tile
+constexpr int HU = 8;             // float4 loads in flight per thread in the histograms
 
 // order-preserving key of a non-NaN float (-0 and +0 compare equal)
 __device__ __forceinline__ uint32_t fkey(float f) {
@@ -78,13 +79,24 @@ __global__ __launch_bounds__(TPB) void sel_hist0(const float* __restrict__ S, lo
   __syncthreads();
   const long long n4 = N >> 2;
   const float4* S4 = reinterpret_cast<const float4*>(S);
-  const long long stride = (long long)gridDim.x * TPB;
-  for (long long i = (long long)blockIdx.x * TPB + threadIdx.x; i < n4; i += stride) {
-    const float4 v = S4[i];
-    atomicAdd(&h[fkey(v.x) >> 21], 1u);
-    atomicAdd(&h[fkey(v.y) >> 21], 1u);
-    atomicAdd(&h[fkey(v.z) >> 21], 1u);
-    atomicAdd(&h[fkey(v.w) >> 21], 1u);
+  // HU independent 16-byte loads in flight per thread before any atomic
+  const long long stride = (long long)gridDim.x * TPB * HU;
+  for (long long i0 = (long long)blockIdx.x * TPB * HU + threadIdx.x; i0 < n4; i0 += stride) {
+    float4 v[HU];
+#pragma unroll
+    for (int u = 0; u < HU; ++u) {
+      const long long i = i0 + (long long)u * TPB;
+      v[u] = i < n4 ? S4[i] : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+#pragma unroll
+    for (int u = 0; u < HU; ++u) {
+      if (i0 + (long long)u * TPB < n4) {
+        atomicAdd(&h[fkey(v[u].x) >> 21], 1u);
+        atomicAdd(&h[fkey(v[u].y) >> 21], 1u);
+        atomicAdd(&h[fkey(v[u].z) >> 21], 1u);
+        atomicAdd(&h[fkey(v[u].w) >> 21], 1u);
+      }
+    }
   }
   if (blockIdx.x == 0)
     for (long long i = (n4 << 2) + threadIdx.x; i < N; i += TPB) atomicAdd(&h[fkey(S[i]) >> 21], 1u);
@@ -111,13 +123,23 @@ __global__ __launch_bounds__(TPB) void sel_hist12(const float* __restrict__ S, l
   };
   const long long n4 = N >> 2;
   const float4* S4 = reinterpret_cast<const float4*>(S);
-  const long long stride = (long long)gridDim.x * TPB;
-  for (long long i = (long long)blockIdx.x * TPB + threadIdx.x; i < n4; i += stride) {
-    const float4 v = S4[i];
-    add(fkey(v.x));
-    add(fkey(v.y));
-    add(fkey(v.z));
-    add(fkey(v.w));
+  const long long stride = (long long)gridDim.x * TPB * HU;
+  for (long long i0 = (long long)blockIdx.x * TPB * HU + threadIdx.x; i0 < n4; i0 += stride) {
+    float4 v[HU];
+#pragma unroll
+    for (int u = 0; u < HU; ++u) {
+      const long long i = i0 + (long long)u * TPB;
+      v[u] = i < n4 ? S4[i] : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+#pragma unroll
+    for (int u = 0; u < HU; ++u) {
+      if (i0 + (long long)u * TPB < n4) {
+        add(fkey(v[u].x));
+        add(fkey(v[u].y));
+        add(fkey(v[u].z));
+        add(fkey(v[u].w));
+      }
+    }
   }
   if (blockIdx.x == 0)
     for (long long i = (n4 << 2) + threadIdx.x; i < N; i += TPB) add(fkey(S[i]));
@@ -437,7 +459,7 @@ hipError_t select_launch(const SelectPlan& p, const float* S, int64_t K, uint8_t
   const SelWs w = carve(p, ws);
   KVZ_LAUNCH("select_init", sel_init, 512, 256, 0, stream, w.hist, w.joint, w.st, (long long)K);
   const long long n4 = p.N / 4;
-  int hb = (int)((n4 + TPB * 8 - 1) / (TPB * 8));
+  int hb = (int)((n4 + TPB * HU - 1) / (TPB * HU));
   if (hb < 1) hb = 1;
   if (hb > 2048) hb = 2048;
   KVZ_LAUNCH("select_hist", sel_hist0, hb, TPB, 0, stream, S, (long long)p.N, w.hist);
