@@ -142,14 +142,17 @@ __global__ __launch_bounds__(256) void attn_pass3_bf16(
     koff[u] = row * D * 2 + (cp ^ (row & SWZ)) * 16;
     voff[u] = row * D * 2 + ((((cp >> 1) ^ (row & VSW)) << 1) | (cp & 1)) * 16;
   }
-  auto copy_tile = [&](int tile, int par) {
+  auto copy_k = [&](int tile, int par) {
     uint4* dk = par ? ldk1 : ldk0;
+#pragma unroll
+    for (int u = 0; u < LOADS; ++u)
+      copy16_to_lds(kbase, seg_bytes, koff[u] + tile * (KT * D * 2), dk + (u * 4 + wave) * 64);
+  };
+  auto copy_v = [&](int tile, int par) {
     uint4* dv = par ? ldv1 : ldv0;
 #pragma unroll
-    for (int u = 0; u < LOADS; ++u) {
-      copy16_to_lds(kbase, seg_bytes, koff[u] + tile * (KT * D * 2), dk + (u * 4 + wave) * 64);
+    for (int u = 0; u < LOADS; ++u)
       copy16_to_lds(vbase, seg_bytes, voff[u] + tile * (KT * D * 2), dv + (u * 4 + wave) * 64);
-    }
   };
   // transposed-read byte offsets of this lane within a V stage, per d tile:
   // key 4*half + c (c = (lane & 15) >> 2), d = 32 dt + 16 mh + 4a
@@ -160,33 +163,48 @@ __global__ __launch_bounds__(256) void attn_pass3_bf16(
   for (int dt = 0; dt < DT; ++dt)
     vrd[dt] = tr_key * D * 2 + (((2 * dt + tr_mh) ^ (tr_key & VSW)) * 32) + tr_a * 8;
 
-  auto body = [&](int tile, int par) {
-    const uint4* sk = par ? ldk1 : ldk0;
+  // accumulator start of a tile's logits: the row's offset, or -inf on keys
+  // the row does not see (only the ragged context tile and the chunk tiles)
+  f32x16 cst;
+#pragma unroll
+  for (int v = 0; v < 16; ++v) cst[v] = start;
+  auto init_of = [&](int tile) -> f32x16 {
+    if (!inchunk && (tile + 1) * KT <= n_c) return cst;
+    f32x16 z;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const int key = tile * KT + acc_row3(v, half);
+      const bool vis = inchunk ? key <= irow : key < n_c;
+      z[v] = vis ? start : -INFINITY;
+    }
+    return z;
+  };
+
+  // Software pipeline over tiles (relative index r, stage parity par = r & 1):
+  // K runs one tile ahead of V.  Iteration r forms p of tile r from its
+  // logits (computed one iteration earlier) between the MFMAs of tile r+1's
+  // logits, then issues tile r's O^T MFMAs; it copies K of tile r+2 into K
+  // stage par and V of tile r+1 into V stage par^1, both last read in
+  // iteration r-1.  Past the range the copies repeat the last tile and the
+  // extra logits are never used.
+  const int last = t_end - 1;
+  auto body = [&](int tile, int par, f32x16& cur, f32x16& nxt) {
+    const uint4* skn = par ? ldk0 : ldk1;
     const char* sv = reinterpret_cast<const char*>(par ? ldv1 : ldv0);
     bf16x8 a[KS];
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) a[ks] = as_bf16x8(sk[n * CH + ((ks * 2 + half) ^ (n & SWZ))]);
-    const bool more = tile + 1 < t_end;
-    if (more) copy_tile(tile + 1, par ^ 1);
-    // logits of the lane's query column over the tile's 32 keys, offset by
-    // the row's -lse2/(scale log2 e)
-    f32x16 c;
-#pragma unroll
-    for (int v = 0; v < 16; ++v) c[v] = start;
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[ks], qr[ks], c, 0, 0, 0);
-    const int key0 = tile * KT;
+    for (int ks = 0; ks < KS; ++ks) a[ks] = as_bf16x8(skn[n * CH + ((ks * 2 + half) ^ (n & SWZ))]);
+    copy_k(min(tile + 2, last), par);
+    copy_v(min(tile + 1, last), par ^ 1);
+    const f32x16 init = init_of(min(tile + 1, last));
     float p[16];
-    if (!inchunk && key0 + KT <= n_c) {
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int v = 0; v < 16; ++v) p[v] = fast_exp2(c[v] * cl2);
-    } else {
+    for (int ks = 0; ks < KS; ++ks) {
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int key = key0 + acc_row3(v, half);
-        const bool vis = inchunk ? key <= irow : key < n_c;
-        p[v] = vis ? fast_exp2(c[v] * cl2) : 0.f;
-      }
+      for (int v = ks * 16 / KS; v < (ks + 1) * 16 / KS; ++v) p[v] = fast_exp2(cur[v] * cl2);
+      nxt = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[ks], qr[ks], ks == 0 ? init : nxt, 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
     }
     bf16x8 pb[2];
 #pragma unroll
@@ -205,21 +223,33 @@ __global__ __launch_bounds__(256) void attn_pass3_bf16(
                                                         o[dt], 0, 0, 0);
       }
     }
-    __builtin_amdgcn_s_waitcnt(0);  // this wave's copies of the next tile have landed
+    __builtin_amdgcn_s_waitcnt(0);  // this wave's copies have landed
     __syncthreads();
   };
 
   if (t_begin < t_end) {
-    copy_tile(t_begin, 0);
+    copy_k(t_begin, 0);
+    copy_k(min(t_begin + 1, last), 1);
+    copy_v(t_begin, 0);
     __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    f32x16 A, B;
+    {
+      const f32x16 init = init_of(t_begin);
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const bf16x8 a = as_bf16x8(ldk0[n * CH + ((ks * 2 + half) ^ (n & SWZ))]);
+        A = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qr[ks], ks == 0 ? init : A, 0, 0, 0);
+      }
+    }
+    __syncthreads();  // every wave has read K stage 0 before it is refilled
+    int tile = t_begin;
+    for (; tile + 1 < t_end; tile += 2) {
+      body(tile, 0, A, B);
+      body(tile + 1, 1, B, A);
+    }
+    if (tile < t_end) body(tile, 0, A, B);
   }
-  __syncthreads();
-  int tile = t_begin;
-  for (; tile + 1 < t_end; tile += 2) {
-    body(tile, 0);
-    body(tile + 1, 1);
-  }
-  if (tile < t_end) body(tile, 0);
 
   // lane (n, half) holds d = 32 dt + 8 vg + 4 half + 0..3 of query row r
   float* op = opart + (((size_t)s * H + h) * R_pad + r) * D;
