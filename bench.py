@@ -115,7 +115,7 @@ def main():
                          "kernel of known size, to scale the HBM traffic counters)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
+        print(f"bench.py: the benchmark runs on one GPU; --gpus {args.gpus} is not supported "
               "(the per-head scoring would shard across GPUs without communication, but no "
               "multi-GPU path is built)", file=sys.stderr)
         sys.exit(2)
