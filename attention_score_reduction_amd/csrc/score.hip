@@ -141,7 +141,10 @@ __device__ __forceinline__ int acc_row(int v, int half) {
 // ---------------------------------------------------------------------------
 template <int D>
 struct P1Shape {
-  static constexpr int NQ = 2;  // query tiles per wave
+  // query tiles per wave: two at d <= 128 (each LDS operand read feeds two
+  // MFMAs); one at d=256, where two would need 300 VGPRs (occupancy 1) and
+  // measured 10% slower
+  static constexpr int NQ = D <= 128 ? 2 : 1;
   static constexpr int ROWS = 4 * 32 * NQ;                     // query rows per workgroup
 };
 
