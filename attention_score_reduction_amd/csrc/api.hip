@@ -58,6 +58,12 @@ namespace {
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 bool head_dim_ok(int d) { return d == 64 || d == 128 || d == 256; }
+// one head's context keys (and values) must fit a buffer resource's 32-bit
+// byte range: the score and output kernels copy them into LDS by buffer
+// loads whose offsets and range are 32-bit
+bool ctx_fits(int n_c, int d) {
+  return n_c <= (1 << 24) && (long long)n_c * d * 2 <= 0x7fffffffLL;
+}
 hipError_t clear_error() { return hipGetLastError(); }
 
 }  // namespace
@@ -77,7 +83,7 @@ const char* kvz_status_string(kvz_status s) {
 
 size_t kvz_score_chunk_workspace(kvz_dtype dt, int H, int G, int n_in, int d, int n_c) {
   if (H < 1 || G < 1 || n_in < 1 || n_c < 1 || (dt != KVZ_BF16 && dt != KVZ_F32)) return 0;
-  if ((long long)G * n_in > (1 << 20) || n_c > (1 << 24)) return 0;
+  if ((long long)G * n_in > (1 << 20) || !ctx_fits(n_c, d)) return 0;
   return score_plan(dt, H, G, n_in, d, n_c).total_bytes;
 }
 
@@ -91,7 +97,7 @@ kvz_status kvz_score_chunk_ex(kvz_dtype dt, kvz_aggregate agg, int H, int G, int
   if (!head_dim_ok(d)) return KVZ_ERR_UNSUPPORTED;
   if (H < 1 || G < 1 || n_in < 1 || n_c < 1 || n_prompt < 0 || n_prompt > n_in)
     return KVZ_ERR_INVALID_ARG;
-  if ((long long)G * n_in > (1 << 20) || n_c > (1 << 24)) return KVZ_ERR_INVALID_ARG;
+  if ((long long)G * n_in > (1 << 20) || !ctx_fits(n_c, d)) return KVZ_ERR_INVALID_ARG;
   if (!q || !k_ctx || !k_in || !S || !ws) return KVZ_ERR_INVALID_ARG;
   if (!aligned16(q) || !aligned16(k_ctx) || !aligned16(k_in) || !aligned16(S))
     return KVZ_ERR_INVALID_ARG;
@@ -114,7 +120,7 @@ kvz_status kvz_score_chunk(kvz_dtype dt, int H, int G, int d, int n_c, int n_pro
 
 size_t kvz_score_chunk_attn_workspace(kvz_dtype dt, int H, int G, int n_in, int d, int n_c) {
   if ((dt != KVZ_BF16 && dt != KVZ_F32) || !head_dim_ok(d) || H < 1 || G < 1 || n_in < 1 ||
-      n_c < 1 || (long long)G * n_in > (1 << 20) || n_c > (1 << 24))
+      n_c < 1 || (long long)G * n_in > (1 << 20) || !ctx_fits(n_c, d))
     return 0;
   const ScorePlan p = score_plan(dt, H, G, n_in, d, n_c);
   return p.total_bytes + attn_plan(dt, p).part_bytes;
@@ -128,7 +134,7 @@ kvz_status kvz_score_chunk_attn(kvz_dtype dt, int H, int G, int d, int n_c, int 
   if (!head_dim_ok(d)) return KVZ_ERR_UNSUPPORTED;
   if (H < 1 || G < 1 || n_in < 1 || n_c < 1 || n_prompt < 0 || n_prompt > n_in)
     return KVZ_ERR_INVALID_ARG;
-  if ((long long)G * n_in > (1 << 20) || n_c > (1 << 24)) return KVZ_ERR_INVALID_ARG;
+  if ((long long)G * n_in > (1 << 20) || !ctx_fits(n_c, d)) return KVZ_ERR_INVALID_ARG;
   if (!q || !k_ctx || !k_in || !v_ctx || !v_in || !S || !O || !ws) return KVZ_ERR_INVALID_ARG;
   if (!aligned16(q) || !aligned16(k_ctx) || !aligned16(k_in) || !aligned16(v_ctx) ||
       !aligned16(v_in) || !aligned16(S) || !aligned16(O))

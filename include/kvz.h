@@ -99,7 +99,9 @@ KVZ_API const char* kvz_status_string(kvz_status s);
  * finite and > 0.  n_prompt is validated (0 <= n_prompt <= n_in) and only
  * documents the row split: every row is a query and is masked the same way.
  *
- * Limits: d in {64, 128, 256}; 1 <= n_in, 1 <= n_c <= 2^24, 1 <= H, 1 <= G,
+ * Limits: d in {64, 128, 256}; 1 <= n_in, 1 <= n_c <= 2^24 with one head's
+ * keys under 2 GiB (n_c * d * 2 <= 2^31 - 1, i.e. n_c <= 4,194,303 at d=256
+ * and 8,388,607 at d=128), 1 <= H, 1 <= G,
  * G * n_in <= 2^20.  Workspace: kvz_score_chunk_workspace() bytes, 256-byte
  * aligned, device memory.
  * ---------------------------------------------------------------------- */

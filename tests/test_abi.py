@@ -79,6 +79,9 @@ def _score(**kw):
     (dict(ws=P(4096 + 64)), kvz.KVZ_ERR_INVALID_ARG), (dict(scale=0.0), kvz.KVZ_ERR_INVALID_ARG),
     (dict(scale=float("nan")), kvz.KVZ_ERR_INVALID_ARG), (dict(scale=-1.0), kvz.KVZ_ERR_INVALID_ARG),
     (dict(wsb=16), kvz.KVZ_ERR_WORKSPACE), (dict(G=1 << 11, n_in=1 << 10), kvz.KVZ_ERR_INVALID_ARG),
+    # one head's keys past 2 GiB (the 32-bit range of the buffer loads)
+    (dict(d=256, n_c=4194304), kvz.KVZ_ERR_INVALID_ARG),
+    (dict(d=128, n_c=8388608), kvz.KVZ_ERR_INVALID_ARG),
 ])
 def test_score_validation(kw, status):
     assert _score(**kw) == status
@@ -99,7 +102,7 @@ def _attn(**kw):
     (dict(vc=None), kvz.KVZ_ERR_INVALID_ARG), (dict(vi=None), kvz.KVZ_ERR_INVALID_ARG),
     (dict(O=None), kvz.KVZ_ERR_INVALID_ARG), (dict(vi=MIS), kvz.KVZ_ERR_INVALID_ARG),
     (dict(O=MIS), kvz.KVZ_ERR_INVALID_ARG), (dict(scale=0.0), kvz.KVZ_ERR_INVALID_ARG),
-    (dict(wsb=16), kvz.KVZ_ERR_WORKSPACE),
+    (dict(wsb=16), kvz.KVZ_ERR_WORKSPACE), (dict(d=256, n_c=4194304), kvz.KVZ_ERR_INVALID_ARG),
 ])
 def test_score_attn_validation(kw, status):
     assert _attn(**kw) == status
@@ -111,6 +114,9 @@ def test_score_attn_workspace_covers_score_workspace():
         s = kvz.kvz_score_chunk_workspace(dt, 8, 4, 2064, d, 131072)
         assert a >= s > 0
     assert kvz.kvz_score_chunk_attn_workspace(kvz.KVZ_BF16, 8, 4, 2064, 96, 131072) == 0
+    assert kvz.kvz_score_chunk_attn_workspace(kvz.KVZ_BF16, 8, 4, 2064, 256, 4194304) == 0
+    assert kvz.kvz_score_chunk_workspace(kvz.KVZ_BF16, 8, 4, 2064, 256, 4194304) == 0
+    assert kvz.kvz_score_chunk_workspace(kvz.KVZ_BF16, 8, 4, 2064, 256, 4194303) > 0
     # exactly the required size passes validation, one byte less does not
     need = kvz.kvz_score_chunk_attn_workspace(kvz.KVZ_BF16, 2, 4, 20, 128, 100)
     assert _attn(wsb=need - 1) == kvz.KVZ_ERR_WORKSPACE
