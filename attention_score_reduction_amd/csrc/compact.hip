@@ -113,8 +113,9 @@ __global__ __launch_bounds__(TPB) void cmp_scatter(
       if (x < total) {
         const int k = x / RC, c = x % RC;
         const int64_t src = (int64_t)list[k] * RC + c;
-        kv[j] = ksrc[src];
-        vv[j] = vsrc[src];
+        // rows are read once: nontemporal loads keep them out of the caches
+        kv[j] = __builtin_nontemporal_load(ksrc + src);
+        vv[j] = __builtin_nontemporal_load(vsrc + src);
       }
     }
 #pragma unroll
