@@ -247,7 +247,9 @@ KVZ_API kvz_status kvz_decode_packed(kvz_dtype dt, int64_t n_heads, int G, int d
  * While enabled, every kernel the library launches is bracketed by a pair of
  * HIP events on its stream.  kvz_prof_read() synchronises those events and
  * returns, for the kernel named `name` ("score_pass1", "score_combine",
- * "score_pass2", "select_*", "compact_*"), the number of launches and the
+ * "score_pass2", "attn_pass3", "attn_reduce", "select_*", "compact_*",
+ * "head_scores", "token_scores", "decode_split", "decode_combine"), the
+ * number of launches and the
  * summed duration in milliseconds since the last enable.  Returns KVZ_OK, or
  * KVZ_ERR_INVALID_ARG for an unknown name.  max_launches bounds the event
  * pool; launches beyond it are not timed.
