@@ -231,6 +231,42 @@ __device__ __forceinline__ long long tile_range(int64_t tile, int tiles_per_head
   return head * (long long)n_c + start;
 }
 
+// Vector layout of a tile (n_c a multiple of 4, so every tile starts 16-byte
+// aligned): in slab u (1024 scores) thread t owns scores u*1024 + 4t .. +3.
+// Scores past the tile's length are flagged invalid.
+constexpr int VSLABS = TILE / (4 * TPB);  // 4
+__device__ __forceinline__ void load_keys4(const float* __restrict__ S, long long base, int e0,
+                                           int len, uint32_t (&k)[4], bool (&ok)[4]) {
+  if (e0 + 3 < len) {
+    const float4 v = *reinterpret_cast<const float4*>(S + base + e0);
+    k[0] = fkey(v.x);
+    k[1] = fkey(v.y);
+    k[2] = fkey(v.z);
+    k[3] = fkey(v.w);
+#pragma unroll
+    for (int c = 0; c < 4; ++c) ok[c] = true;
+  } else {
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      ok[c] = e0 + c < len;
+      k[c] = ok[c] ? fkey(S[base + e0 + c]) : 0u;
+    }
+  }
+}
+// mask bytes of 4 consecutive scores (one 32-bit store when all are valid)
+__device__ __forceinline__ void store_mask4(uint8_t* __restrict__ mask, long long base, int e0,
+                                            const bool (&keep)[4], const bool (&ok)[4]) {
+  if (ok[3]) {
+    const uint32_t w = (keep[0] ? 1u : 0u) | (keep[1] ? 1u << 8 : 0u) |
+                       (keep[2] ? 1u << 16 : 0u) | (keep[3] ? 1u << 24 : 0u);
+    *reinterpret_cast<uint32_t*>(mask + base + e0) = w;
+  } else {
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+      if (ok[c]) mask[base + e0 + c] = keep[c] ? 1 : 0;
+  }
+}
+
 __device__ __forceinline__ uint32_t block_sum_u32(uint32_t v, uint32_t* red) {
   for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off);
   const int w = threadIdx.x >> 6;
@@ -253,10 +289,21 @@ __global__ __launch_bounds__(TPB) void sel_tile_count(const float* __restrict__ 
   const long long base = tile_range(tile, tiles_per_head, n_c, len);
   const uint32_t tau = st->tau;
   uint32_t eq = 0;
+  if ((n_c & 3) == 0) {
 #pragma unroll
-  for (int u = 0; u < PER_T; ++u) {
-    const int e = u * TPB + threadIdx.x;
-    if (e < len) eq += fkey(S[base + e]) == tau;
+    for (int u = 0; u < VSLABS; ++u) {
+      uint32_t k[4];
+      bool ok[4];
+      load_keys4(S, base, u * 4 * TPB + 4 * threadIdx.x, len, k, ok);
+#pragma unroll
+      for (int c = 0; c < 4; ++c) eq += ok[c] && k[c] == tau;
+    }
+  } else {
+#pragma unroll
+    for (int u = 0; u < PER_T; ++u) {
+      const int e = u * TPB + threadIdx.x;
+      if (e < len) eq += fkey(S[base + e]) == tau;
+    }
   }
   eq = block_sum_u32(eq, red);
   if (threadIdx.x == 0) eqc[tile] = eq;
@@ -318,7 +365,54 @@ __global__ __launch_bounds__(TPB) void sel_mask(const float* __restrict__ S,
   const bool split = st->split_ties != 0;
   const int t = threadIdx.x, lane = t & 63, w = t >> 6;
   uint32_t kept = 0;
-  if (!split) {
+  if ((n_c & 3) == 0) {
+    // vector layout; ties are ranked in flat order: earlier slabs, then
+    // earlier threads of the slab (a ballot per bit of the per-thread tie
+    // count, 0..4), then earlier scores of the thread
+    const long long need_eq = split ? st->krem[3] : 0;
+    const long long eb = split ? eqbase[tile] : 0;
+    long long run = 0;
+#pragma unroll
+    for (int u = 0; u < VSLABS; ++u) {
+      const int e0 = u * 4 * TPB + 4 * t;
+      uint32_t k[4];
+      bool ok[4], keep[4];
+      load_keys4(S, base, e0, len, k, ok);
+      if (!split) {
+#pragma unroll
+        for (int c = 0; c < 4; ++c) keep[c] = ok[c] && k[c] >= tau;
+      } else {
+        bool eq[4];
+        uint32_t cnt = 0;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          eq[c] = ok[c] && k[c] == tau;
+          cnt += eq[c];
+        }
+        uint32_t below = 0, wsum = 0;
+        const unsigned long long lt = (1ull << lane) - 1ull;
+#pragma unroll
+        for (int bit = 0; bit < 3; ++bit) {
+          const unsigned long long b = __ballot((cnt >> bit) & 1u);
+          below += (uint32_t)__popcll(b & lt) << bit;
+          wsum += (uint32_t)__popcll(b) << bit;
+        }
+        if (lane == 0) wtot[u][w] = wsum;
+        __syncthreads();
+        long long before = run + below;
+        for (int ww = 0; ww < w; ++ww) before += wtot[u][ww];
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          keep[c] = ok[c] && (k[c] > tau || (eq[c] && eb + before < need_eq));
+          before += eq[c];
+        }
+        run += wtot[u][0] + wtot[u][1] + wtot[u][2] + wtot[u][3];
+      }
+      store_mask4(mask, base, e0, keep, ok);
+#pragma unroll
+      for (int c = 0; c < 4; ++c) kept += keep[c];
+    }
+  } else if (!split) {
 #pragma unroll
     for (int u = 0; u < PER_T; ++u) {
       const int e = u * TPB + t;
