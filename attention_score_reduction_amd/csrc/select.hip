@@ -42,6 +42,11 @@ constexpr int TILE = 4096;        // scores per mask tile (within one head)
 constexpr int TPB = 256;          // threads per block
 constexpr int PER_T = TILE / TPB; // 16 scores per thread per tile
 constexpr int HU = 8;             // float4 loads in flight per thread in the histograms
+constexpr int HR = 4;             // lane-replicated copies of each LDS histogram bin
+#ifndef KVZ_HB_MAX
+#define KVZ_HB_MAX 512
+#endif
+constexpr int HB_MAX = KVZ_HB_MAX; // histogram workgroups per pass
 
 // order-preserving key of a non-NaN float (-0 and +0 compare equal)
 __device__ __forceinline__ uint32_t fkey(float f) {
@@ -74,9 +79,13 @@ __global__ void sel_init(uint32_t* __restrict__ hist, uint32_t* __restrict__ joi
 // full read, histogram of the top 11 bits
 __global__ __launch_bounds__(TPB) void sel_hist0(const float* __restrict__ S, long long N,
                                                  uint32_t* __restrict__ hist) {
-  __shared__ uint32_t h[BINS];
-  for (int b = threadIdx.x; b < BINS; b += TPB) h[b] = 0;
+  // HR copies of every bin in consecutive banks, copy = lane % HR: lanes of
+  // a wave that hit the same bin (scores crowd into few bins) spread over HR
+  // banks instead of serialising on one
+  __shared__ uint32_t h[BINS * HR];
+  for (int b = threadIdx.x; b < BINS * HR; b += TPB) h[b] = 0;
   __syncthreads();
+  const uint32_t rep = threadIdx.x & (HR - 1);
   const long long n4 = N >> 2;
   const float4* S4 = reinterpret_cast<const float4*>(S);
   // HU independent 16-byte loads in flight per thread before any atomic
@@ -91,18 +100,23 @@ __global__ __launch_bounds__(TPB) void sel_hist0(const float* __restrict__ S, lo
 #pragma unroll
     for (int u = 0; u < HU; ++u) {
       if (i0 + (long long)u * TPB < n4) {
-        atomicAdd(&h[fkey(v[u].x) >> 21], 1u);
-        atomicAdd(&h[fkey(v[u].y) >> 21], 1u);
-        atomicAdd(&h[fkey(v[u].z) >> 21], 1u);
-        atomicAdd(&h[fkey(v[u].w) >> 21], 1u);
+        atomicAdd(&h[(fkey(v[u].x) >> 21) * HR + rep], 1u);
+        atomicAdd(&h[(fkey(v[u].y) >> 21) * HR + rep], 1u);
+        atomicAdd(&h[(fkey(v[u].z) >> 21) * HR + rep], 1u);
+        atomicAdd(&h[(fkey(v[u].w) >> 21) * HR + rep], 1u);
       }
     }
   }
   if (blockIdx.x == 0)
-    for (long long i = (n4 << 2) + threadIdx.x; i < N; i += TPB) atomicAdd(&h[fkey(S[i]) >> 21], 1u);
+    for (long long i = (n4 << 2) + threadIdx.x; i < N; i += TPB)
+      atomicAdd(&h[(fkey(S[i]) >> 21) * HR + rep], 1u);
   __syncthreads();
-  for (int b = threadIdx.x; b < BINS; b += TPB)
-    if (h[b]) atomicAdd(&hist[b], h[b]);
+  for (int b = threadIdx.x; b < BINS; b += TPB) {
+    uint32_t c = 0;
+#pragma unroll
+    for (int r = 0; r < HR; ++r) c += h[b * HR + r];
+    if (c) atomicAdd(&hist[b], c);
+  }
 }
 
 // full read, scores whose top bits equal b0: LDS histogram of bits 20..10 and
@@ -111,13 +125,14 @@ __global__ __launch_bounds__(TPB) void sel_hist12(const float* __restrict__ S, l
                                                   uint32_t* __restrict__ hist1,
                                                   uint32_t* __restrict__ joint,
                                                   const SelState* __restrict__ st) {
-  __shared__ uint32_t h[BINS];
-  for (int b = threadIdx.x; b < BINS; b += TPB) h[b] = 0;
+  __shared__ uint32_t h[BINS * HR];  // lane-replicated, as in sel_hist0
+  for (int b = threadIdx.x; b < BINS * HR; b += TPB) h[b] = 0;
   __syncthreads();
   const uint32_t b0 = st->b0;
+  const uint32_t rep = threadIdx.x & (HR - 1);
   auto add = [&](uint32_t k) {
     if ((k >> 21) == b0) {
-      atomicAdd(&h[(k >> 10) & 0x7FF], 1u);
+      atomicAdd(&h[((k >> 10) & 0x7FF) * HR + rep], 1u);
       atomicAdd(&joint[k & (JBINS - 1)], 1u);
     }
   };
@@ -144,8 +159,12 @@ __global__ __launch_bounds__(TPB) void sel_hist12(const float* __restrict__ S, l
   if (blockIdx.x == 0)
     for (long long i = (n4 << 2) + threadIdx.x; i < N; i += TPB) add(fkey(S[i]));
   __syncthreads();
-  for (int b = threadIdx.x; b < BINS; b += TPB)
-    if (h[b]) atomicAdd(&hist1[b], h[b]);
+  for (int b = threadIdx.x; b < BINS; b += TPB) {
+    uint32_t c = 0;
+#pragma unroll
+    for (int r = 0; r < HR; ++r) c += h[b * HR + r];
+    if (c) atomicAdd(&hist1[b], c);
+  }
 }
 
 // Suffix search over NB bins held by one 256-thread workgroup (NB/256 bins per
@@ -553,7 +572,11 @@ hipError_t select_launch(const SelectPlan& p, const float* S, int64_t K, uint8_t
   const SelWs w = carve(p, ws);
   KVZ_LAUNCH("select_init", sel_init, 512, 256, 0, stream, w.hist, w.joint, w.st, (long long)K);
   const long long n4 = p.N / 4;
-  int hb = (int)((n4 + TPB * HU - 1) / (TPB * HU));
+  // at most HB_MAX workgroups, each looping over its share: the LDS
+  // histogram's clearing and flush are paid once per workgroup
+  long long hbl = (n4 + TPB * HU - 1) / (TPB * HU);
+  if (hbl > HB_MAX) hbl = HB_MAX;
+  int hb = (int)hbl;
   if (hb < 1) hb = 1;
   if (hb > 2048) hb = 2048;
   KVZ_LAUNCH("select_hist", sel_hist0, hb, TPB, 0, stream, S, (long long)p.N, w.hist);
