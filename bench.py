@@ -211,8 +211,10 @@ def main():
     hbm_bytes = {
         # gather K and V rows, write them packed, idx, read the mask
         "compact_scatter": K * (4 * row_bytes + 4) + N,
-        # three histogram rounds, tile counts, mask pass (reads of S) + mask write
-        "select_total": 5 * 4 * N + N,
+        # reads of S: two radix-histogram passes, the tie count per tile (it
+        # runs when the K-th boundary splits a run of equal scores, as fp32
+        # maxima collide on these caches) and the mask pass; plus the mask write
+        "select_total": 4 * 4 * N + N,
     }
     hbm = {}
     if "compact_scatter" in kern:
