@@ -37,7 +37,12 @@ template <int D>
 struct G3 {
   static constexpr int KS = D / 16, CH = D / 8, SWZ = (CH < 16 ? CH : 16) - 1, DT = D / 32;
   static constexpr int NB = D / 16;                  // 32-byte blocks per V row
-  static constexpr int VSW = (NB < 8 ? NB : 8) - 1;  // V block swizzle mask
+  // V block swizzle of key k: block ^ vsw(k), vsw(k) = 2 (k & 3) (within the
+  // row's NB blocks).  A 16-lane group of transposing reads takes one block
+  // (2 dt + mh) of four keys k & 3 = 0..3: even XOR offsets keep those four
+  // blocks distinct, and the two groups of a half-wave (mh = 0, 1) on even
+  // and odd blocks, so 32 lanes read 64 distinct banks
+  static constexpr int VSW = NB - 1;
 };
 
 __device__ __forceinline__ int acc_row3(int v, int half) {
@@ -132,7 +137,7 @@ __global__ __launch_bounds__(256) void attn_pass3_bf16(
   for (int t = 0; t < DT; ++t) o[t] = f32x16{};
 
   // copies: slot p of a stage holds key p / CH; for K its 16-byte chunk
-  // (p % CH) ^ (key & SWZ), for V its 32-byte block ((p % CH) / 2) ^ (key & VSW)
+  // (p % CH) ^ (key & SWZ), for V its 32-byte block ((p % CH) / 2) ^ vsw(key)
   const int seg_bytes = nkeys * D * 2;
   int koff[LOADS], voff[LOADS];
 #pragma unroll
@@ -140,7 +145,7 @@ __global__ __launch_bounds__(256) void attn_pass3_bf16(
     const int slot = (u * 4 + wave) * 64 + lane;
     const int row = slot / CH, cp = slot % CH;
     koff[u] = row * D * 2 + (cp ^ (row & SWZ)) * 16;
-    voff[u] = row * D * 2 + ((((cp >> 1) ^ (row & VSW)) << 1) | (cp & 1)) * 16;
+    voff[u] = row * D * 2 + ((((cp >> 1) ^ (((row & 3) << 1) & VSW)) << 1) | (cp & 1)) * 16;
   }
   auto copy_k = [&](int tile, int par) {
     uint4* dk = par ? ldk1 : ldk0;
@@ -161,7 +166,7 @@ __global__ __launch_bounds__(256) void attn_pass3_bf16(
   int vrd[DT];
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt)
-    vrd[dt] = tr_key * D * 2 + (((2 * dt + tr_mh) ^ (tr_key & VSW)) * 32) + tr_a * 8;
+    vrd[dt] = tr_key * D * 2 + (((2 * dt + tr_mh) ^ (((tr_key & 3) << 1) & VSW)) * 32) + tr_a * 8;
 
   // accumulator start of a tile's logits: the row's offset, or -inf on keys
   // the row does not see (only the ragged context tile and the chunk tiles)
