@@ -289,12 +289,12 @@ kvz_status kvz_prof_read(const char* name, int64_t* launches, double* total_ms) 
   int64_t n = 0;
   double ms = 0.0;
   bool known = false;
-  static const char* kNames[] = {"score_pass1",   "score_combine",     "score_pass2",
-                                 "select_empty",  "select_init",       "select_hist",
-                                 "select_pick",   "select_tile_count", "select_scan",
-                                 "select_mask",   "compact_count",     "compact_scan",
+  static const char* kNames[] = {"score_pass1",     "score_combine",  "score_pass2",
+                                 "select_empty",    "select_init",    "select_hist",
+                                 "select_pick",     "select_fixup",   "select_scan",
+                                 "select_mask",     "compact_count",  "compact_scan",
                                  "compact_scatter", "head_scores",    "token_scores",
-                                 "decode_split",  "decode_combine",    "attn_pass3",
+                                 "decode_split",    "decode_combine", "attn_pass3",
                                  "attn_reduce"};
   for (const char* k : kNames) known |= strcmp(k, name) == 0;
   if (!known) return KVZ_ERR_INVALID_ARG;

@@ -11,7 +11,8 @@
 // exactly K.  Everything stays on the device (no host synchronisation) and
 // every atomic is an integer add, so the result is deterministic.
 //
-// Passes over S (N floats): three in the common case.
+// Passes over S (N floats): three, plus a re-read of the few tiles whose
+// ties are kept when the K-th boundary splits a run of equal scores.
 //   sel_init       zero the histograms and the search state
 //   sel_hist0      full read: histogram of bits 31..21 (2048 bins)
 //   sel_pick<0>    the top-level bin b0 holding the K-th largest
@@ -21,12 +22,14 @@
 //   sel_pick<1>    bin b1 of bits 20..10
 //   sel_pick2      bin b2 of bits 9..0 from the joint histogram row b1:
 //                  tau, the number of ties to keep, and whether every
-//                  score equal to tau is kept (the common case)
-//   sel_tile_count full read, only when ties are split: #(> tau), #(== tau)
-//                  per 4096-score tile
+//                  score equal to tau is kept (the common case for
+//                  continuous scores)
+//   sel_mask       full read + mask write: keep > tau (>= tau when no tie
+//                  is dropped); kept and tied counts per 4096-score tile
 //   sel_eq_scan    only when ties are split: ties in all earlier tiles
-//   sel_mask       full read + mask write: keep flags (tie ranks by wave
-//                  ballots), kept count per tile
+//   sel_fixup      only when ties are split, and only tiles holding kept
+//                  ties: re-read the tile, rank its ties in flat order (wave
+//                  ballots), set their mask bytes, add them to its count
 //   sel_heads      per-head budgets and their exclusive scan, tau
 #include <math.h>
 
@@ -296,55 +299,122 @@ __device__ __forceinline__ uint32_t block_sum_u32(uint32_t v, uint32_t* red) {
   return s;
 }
 
-// only when ties are split: #(== tau) per tile (the tie ranks need them)
-__global__ __launch_bounds__(TPB) void sel_tile_count(const float* __restrict__ S,
-                                                      const SelState* __restrict__ st,
-                                                      uint32_t* __restrict__ eqc,
-                                                      int tiles_per_head, int n_c) {
-  if (!st->split_ties) return;
+// one workgroup of 1024 threads: exclusive scans of block sums
+constexpr int SCAN_T = 1024;
+constexpr int SCAN_W = SCAN_T / 64;
+
+// Exclusive scan of one value per thread over the workgroup: shuffle scans
+// within each wave, then one wave scans the SCAN_W wave totals.  buf holds
+// SCAN_W entries; *total gets the sum of all values.  32-bit: the callers
+// scan per-tile counts whose sum is at most N < 2^31.
+__device__ uint32_t block_exclusive_scan(uint32_t v, uint32_t* buf, uint32_t* total) {
+  const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+  uint32_t x = v;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const uint32_t y = __shfl_up(x, off);
+    if (lane >= off) x += y;
+  }
+  if (lane == 63) buf[w] = x;
+  __syncthreads();
+  if (w == 0) {
+    uint32_t y = lane < SCAN_W ? buf[lane] : 0u;
+#pragma unroll
+    for (int off = 1; off < SCAN_W; off <<= 1) {
+      const uint32_t z = __shfl_up(y, off);
+      if (lane >= off) y += z;
+    }
+    if (lane < SCAN_W) buf[lane] = y;
+  }
+  __syncthreads();
+  const uint32_t before = (w ? buf[w - 1] : 0u) + x - v;
+  *total = buf[SCAN_W - 1];
+  __syncthreads();  // buf may be reused at once
+  return before;
+}
+
+// Exclusive scan of n per-tile counts by one SCAN_T workgroup, SPT
+// consecutive tiles per thread per round; out(i, prefix) is called for every
+// tile.  Returns the sum of all counts.
+template <typename Out>
+__device__ long long scan_tiles(const uint32_t* __restrict__ cnt, int64_t n, uint32_t* buf,
+                                Out out) {
+  constexpr int SPT = 8;
+  const int t = threadIdx.x;
+  uint32_t carry = 0;
+  for (int64_t r0 = 0; r0 < n; r0 += (int64_t)SCAN_T * SPT) {
+    const int64_t i0 = r0 + (int64_t)t * SPT;
+    uint32_t v[SPT];
+    uint32_t mine = 0;
+#pragma unroll
+    for (int e = 0; e < SPT; ++e) {
+      v[e] = i0 + e < n ? cnt[i0 + e] : 0u;
+      mine += v[e];
+    }
+    uint32_t total;
+    uint32_t run = carry + block_exclusive_scan(mine, buf, &total);
+#pragma unroll
+    for (int e = 0; e < SPT; ++e) {
+      if (i0 + e < n) out(i0 + e, (long long)run);
+      run += v[e];
+    }
+    carry += total;
+  }
+  return carry;
+}
+
+// Mask of one tile: keep scores > tau, and == tau as well when every tie is
+// kept.  When ties are split they are left out here and counted per tile;
+// sel_fixup adds the first ones in flat order.
+__global__ __launch_bounds__(TPB) void sel_mask(const float* __restrict__ S,
+                                                const SelState* __restrict__ st,
+                                                uint8_t* __restrict__ mask,
+                                                uint32_t* __restrict__ keptc,
+                                                uint32_t* __restrict__ eqc, int tiles_per_head,
+                                                int n_c) {
   __shared__ uint32_t red[4];
   const int64_t tile = blockIdx.x;
   int len;
   const long long base = tile_range(tile, tiles_per_head, n_c, len);
   const uint32_t tau = st->tau;
-  uint32_t eq = 0;
+  const bool all_eq = st->split_ties == 0;
+  const int t = threadIdx.x;
+  uint32_t kept = 0, eq = 0;
   if ((n_c & 3) == 0) {
 #pragma unroll
     for (int u = 0; u < VSLABS; ++u) {
+      const int e0 = u * 4 * TPB + 4 * t;
       uint32_t k[4];
-      bool ok[4];
-      load_keys4(S, base, u * 4 * TPB + 4 * threadIdx.x, len, k, ok);
+      bool ok[4], keep[4];
+      load_keys4(S, base, e0, len, k, ok);
 #pragma unroll
-      for (int c = 0; c < 4; ++c) eq += ok[c] && k[c] == tau;
+      for (int c = 0; c < 4; ++c) {
+        const bool is_eq = ok[c] && k[c] == tau;
+        keep[c] = ok[c] && (k[c] > tau || (all_eq && is_eq));
+        kept += keep[c];
+        eq += is_eq;
+      }
+      store_mask4(mask, base, e0, keep, ok);
     }
   } else {
 #pragma unroll
     for (int u = 0; u < PER_T; ++u) {
-      const int e = u * TPB + threadIdx.x;
-      if (e < len) eq += fkey(S[base + e]) == tau;
+      const int e = u * TPB + t;
+      if (e < len) {
+        const uint32_t k = fkey(S[base + e]);
+        const bool keep = k > tau || (all_eq && k == tau);
+        mask[base + e] = keep ? 1 : 0;
+        kept += keep;
+        eq += k == tau;
+      }
     }
   }
-  eq = block_sum_u32(eq, red);
-  if (threadIdx.x == 0) eqc[tile] = eq;
-}
-
-// one workgroup of 1024 threads: exclusive scan of block sums
-constexpr int SCAN_T = 1024;
-
-__device__ long long block_exclusive_scan(long long v, long long* buf, long long* total) {
-  const int t = threadIdx.x;
-  buf[t] = v;
-  __syncthreads();
-  for (int off = 1; off < SCAN_T; off <<= 1) {
-    const long long add = t >= off ? buf[t - off] : 0;
-    __syncthreads();
-    buf[t] += add;
-    __syncthreads();
+  // both counts are at most TILE < 2^16: one sum of kept + 2^16 * eq
+  const uint32_t both = block_sum_u32(kept | (eq << 16), red);
+  if (t == 0) {
+    keptc[tile] = both & 0xFFFFu;
+    eqc[tile] = both >> 16;
   }
-  const long long incl = buf[t];
-  *total = buf[SCAN_T - 1];
-  __syncthreads();
-  return incl - v;
 }
 
 // only when ties are split: ties in all tiles before each tile
@@ -353,158 +423,121 @@ __global__ __launch_bounds__(SCAN_T) void sel_eq_scan(const SelState* __restrict
                                                       long long* __restrict__ eqbase,
                                                       int64_t n_tiles) {
   if (!st->split_ties) return;
-  __shared__ long long buf[SCAN_T];
-  const int t = threadIdx.x;
-  const int64_t per = (n_tiles + SCAN_T - 1) / SCAN_T;
-  const int64_t b0 = (int64_t)t * per, b1 = min(n_tiles, b0 + per);
-  long long mine = 0;
-  for (int64_t i = b0; i < b1; ++i) mine += eqc[i];
-  long long total;
-  long long run = block_exclusive_scan(mine, buf, &total);
-  for (int64_t i = b0; i < b1; ++i) {
-    eqbase[i] = run;
-    run += eqc[i];
-  }
+  __shared__ uint32_t buf[SCAN_W];
+  scan_tiles(eqc, n_tiles, buf, [&](int64_t i, long long before) { eqbase[i] = before; });
 }
 
-// Mask of one tile; scores in element order e = u*256 + t.  Ties are ranked
-// (wave ballots + per-wave totals) only when they are split.
-__global__ __launch_bounds__(TPB) void sel_mask(const float* __restrict__ S,
-                                                const SelState* __restrict__ st,
-                                                const long long* __restrict__ eqbase,
-                                                uint8_t* __restrict__ mask,
-                                                uint32_t* __restrict__ keptc, int tiles_per_head,
-                                                int n_c) {
+// Only when ties are split, and only in tiles that hold ties while the ties
+// of all earlier tiles leave part of the quota (K - #greater): rank the
+// tile's ties in flat order and set the mask bytes of the kept ones.
+__global__ __launch_bounds__(TPB) void sel_fixup(const float* __restrict__ S,
+                                                 const SelState* __restrict__ st,
+                                                 const uint32_t* __restrict__ eqc,
+                                                 const long long* __restrict__ eqbase,
+                                                 uint8_t* __restrict__ mask,
+                                                 uint32_t* __restrict__ keptc, int tiles_per_head,
+                                                 int n_c) {
+  if (!st->split_ties) return;
+  const int64_t tile = blockIdx.x;
+  if (eqc[tile] == 0) return;
+  const long long need_eq = st->krem[3];
+  const long long eb = eqbase[tile];
+  if (eb >= need_eq) return;
   __shared__ uint32_t wtot[PER_T][4];
   __shared__ uint32_t red[4];
-  const int64_t tile = blockIdx.x;
   int len;
   const long long base = tile_range(tile, tiles_per_head, n_c, len);
   const uint32_t tau = st->tau;
-  const bool split = st->split_ties != 0;
   const int t = threadIdx.x, lane = t & 63, w = t >> 6;
-  uint32_t kept = 0;
+  const unsigned long long lt = (1ull << lane) - 1ull;
+  uint32_t added = 0;
+  long long run = 0;  // ties in earlier slabs (rows) of this tile
   if ((n_c & 3) == 0) {
-    // vector layout; ties are ranked in flat order: earlier slabs, then
-    // earlier threads of the slab (a ballot per bit of the per-thread tie
-    // count, 0..4), then earlier scores of the thread
-    const long long need_eq = split ? st->krem[3] : 0;
-    const long long eb = split ? eqbase[tile] : 0;
-    long long run = 0;
+    // vector layout: earlier slabs, then earlier threads of the slab (a
+    // ballot per bit of the per-thread tie count, 0..4), then earlier
+    // scores of the thread
 #pragma unroll
     for (int u = 0; u < VSLABS; ++u) {
       const int e0 = u * 4 * TPB + 4 * t;
       uint32_t k[4];
-      bool ok[4], keep[4];
+      bool ok[4], eq[4];
       load_keys4(S, base, e0, len, k, ok);
-      if (!split) {
+      uint32_t cnt = 0;
 #pragma unroll
-        for (int c = 0; c < 4; ++c) keep[c] = ok[c] && k[c] >= tau;
-      } else {
-        bool eq[4];
-        uint32_t cnt = 0;
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          eq[c] = ok[c] && k[c] == tau;
-          cnt += eq[c];
-        }
-        uint32_t below = 0, wsum = 0;
-        const unsigned long long lt = (1ull << lane) - 1ull;
-#pragma unroll
-        for (int bit = 0; bit < 3; ++bit) {
-          const unsigned long long b = __ballot((cnt >> bit) & 1u);
-          below += (uint32_t)__popcll(b & lt) << bit;
-          wsum += (uint32_t)__popcll(b) << bit;
-        }
-        if (lane == 0) wtot[u][w] = wsum;
-        __syncthreads();
-        long long before = run + below;
-        for (int ww = 0; ww < w; ++ww) before += wtot[u][ww];
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          keep[c] = ok[c] && (k[c] > tau || (eq[c] && eb + before < need_eq));
-          before += eq[c];
-        }
-        run += wtot[u][0] + wtot[u][1] + wtot[u][2] + wtot[u][3];
+      for (int c = 0; c < 4; ++c) {
+        eq[c] = ok[c] && k[c] == tau;
+        cnt += eq[c];
       }
-      store_mask4(mask, base, e0, keep, ok);
+      uint32_t below = 0, wsum = 0;
 #pragma unroll
-      for (int c = 0; c < 4; ++c) kept += keep[c];
-    }
-  } else if (!split) {
-#pragma unroll
-    for (int u = 0; u < PER_T; ++u) {
-      const int e = u * TPB + t;
-      if (e < len) {
-        const bool keep = fkey(S[base + e]) >= tau;
-        mask[base + e] = keep ? 1 : 0;
-        kept += keep;
+      for (int bit = 0; bit < 3; ++bit) {
+        const unsigned long long bb = __ballot((cnt >> bit) & 1u);
+        below += (uint32_t)__popcll(bb & lt) << bit;
+        wsum += (uint32_t)__popcll(bb) << bit;
       }
+      if (lane == 0) wtot[u][w] = wsum;
+      __syncthreads();
+      long long before = eb + run + below;
+      for (int ww = 0; ww < w; ++ww) before += wtot[u][ww];
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        if (eq[c]) {
+          if (before < need_eq) {
+            mask[base + e0 + c] = 1;
+            ++added;
+          }
+          ++before;
+        }
+      }
+      run += wtot[u][0] + wtot[u][1] + wtot[u][2] + wtot[u][3];
     }
   } else {
-    const long long need_eq = st->krem[3];
-    uint32_t kk[PER_T];
-    bool eqf[PER_T];
+    // scalar layout: element e = u*256 + t
 #pragma unroll
     for (int u = 0; u < PER_T; ++u) {
       const int e = u * TPB + t;
-      kk[u] = e < len ? fkey(S[base + e]) : 0u;
-      eqf[u] = e < len && kk[u] == tau;
-      const unsigned long long b = __ballot(eqf[u]);
-      if (lane == 0) wtot[u][w] = (uint32_t)__popcll(b);
-    }
-    __syncthreads();
-    const long long eb = eqbase[tile];
-    long long run = 0;
-#pragma unroll
-    for (int u = 0; u < PER_T; ++u) {
-      const int e = u * TPB + t;
-      const unsigned long long b = __ballot(eqf[u]);
-      long long before = run;
+      const bool eq = e < len && fkey(S[base + e]) == tau;
+      const unsigned long long bb = __ballot(eq);
+      if (lane == 0) wtot[u][w] = (uint32_t)__popcll(bb);
+      __syncthreads();
+      long long before = eb + run + __popcll(bb & lt);
       for (int ww = 0; ww < w; ++ww) before += wtot[u][ww];
-      before += __popcll(b & ((1ull << lane) - 1ull));
-      if (e < len) {
-        const bool keep = kk[u] > tau || (eqf[u] && eb + before < need_eq);
-        mask[base + e] = keep ? 1 : 0;
-        kept += keep;
+      if (eq && before < need_eq) {
+        mask[base + e] = 1;
+        ++added;
       }
       run += wtot[u][0] + wtot[u][1] + wtot[u][2] + wtot[u][3];
     }
   }
-  kept = block_sum_u32(kept, red);
-  if (t == 0) keptc[tile] = kept;
+  added = block_sum_u32(added, red);
+  if (t == 0) keptc[tile] += added;
 }
 
-// one workgroup: per-head budgets (sum of the head's tile counts) and their
-// exclusive scan; tau
+// one workgroup: head offsets from a scan of the per-tile kept counts (a
+// head's tiles are consecutive, so its offset is the prefix at its first
+// tile), the total, tau
 __global__ __launch_bounds__(SCAN_T) void sel_heads(const SelState* __restrict__ st,
                                                     const uint32_t* __restrict__ keptc,
                                                     int64_t* __restrict__ head_offsets,
                                                     float* __restrict__ tau_out,
                                                     int tiles_per_head, int64_t n_heads) {
-  __shared__ long long buf[SCAN_T];
-  const int t = threadIdx.x;
-  const int64_t hper = (n_heads + SCAN_T - 1) / SCAN_T;
-  const int64_t h0 = (int64_t)t * hper, h1 = min(n_heads, h0 + hper);
-  long long hs = 0;
-  for (int64_t h = h0; h < h1; ++h) {
-    const uint32_t* kp = keptc + h * tiles_per_head;
-    long long s = 0;
-#pragma unroll 8
-    for (int k = 0; k < tiles_per_head; ++k) s += kp[k];
-    hs += s;
-  }
-  long long total;
-  long long hrun = block_exclusive_scan(hs, buf, &total);
-  for (int64_t h = h0; h < h1; ++h) {
-    head_offsets[h] = hrun;
-    const uint32_t* kp = keptc + h * tiles_per_head;
-    long long s = 0;
-#pragma unroll 8
-    for (int k = 0; k < tiles_per_head; ++k) s += kp[k];
-    hrun += s;
-  }
-  if (t == 0) {
+  __shared__ uint32_t buf[SCAN_W];
+  // this thread's next head start at or after the tile being written (one
+  // division per round: a thread's tiles are consecutive within a round)
+  int64_t hb = 0, nb = -1;
+  const long long total = scan_tiles(keptc, n_heads * tiles_per_head, buf,
+                                     [&](int64_t i, long long before) {
+                                       if (nb < i) {
+                                         hb = (i + tiles_per_head - 1) / tiles_per_head;
+                                         nb = hb * tiles_per_head;
+                                       }
+                                       if (i == nb) {
+                                         head_offsets[hb] = before;
+                                         ++hb;
+                                         nb += tiles_per_head;
+                                       }
+                                     });
+  if (threadIdx.x == 0) {
     head_offsets[n_heads] = total;
     *tau_out = key_to_float(st->tau);
   }
@@ -585,11 +618,11 @@ hipError_t select_launch(const SelectPlan& p, const float* S, int64_t K, uint8_t
              w.joint, w.st);
   KVZ_LAUNCH("select_pick", sel_pick<1>, 1, TPB, 0, stream, w.hist, w.st);
   KVZ_LAUNCH("select_pick", sel_pick2, 1, TPB, 0, stream, w.joint, w.st);
-  KVZ_LAUNCH("select_tile_count", sel_tile_count, (unsigned)p.n_tiles, TPB, 0, stream, S, w.st,
+  KVZ_LAUNCH("select_mask", sel_mask, (unsigned)p.n_tiles, TPB, 0, stream, S, w.st, mask, w.keptc,
              w.eqc, p.tiles_per_head, p.n_c);
   KVZ_LAUNCH("select_scan", sel_eq_scan, 1, SCAN_T, 0, stream, w.st, w.eqc, w.eqbase, p.n_tiles);
-  KVZ_LAUNCH("select_mask", sel_mask, (unsigned)p.n_tiles, TPB, 0, stream, S, w.st, w.eqbase, mask,
-             w.keptc, p.tiles_per_head, p.n_c);
+  KVZ_LAUNCH("select_fixup", sel_fixup, (unsigned)p.n_tiles, TPB, 0, stream, S, w.st, w.eqc,
+             w.eqbase, mask, w.keptc, p.tiles_per_head, p.n_c);
   KVZ_LAUNCH("select_scan", sel_heads, 1, SCAN_T, 0, stream, w.st, w.keptc, head_offsets, tau,
              p.tiles_per_head, p.n_heads);
   return hipGetLastError();

@@ -196,7 +196,7 @@ def main():
     ms_per_step = (t1 - t0) * 1000.0 / args.steps
 
     names = ["score_pass1", "score_combine", "score_pass2", "select_init", "select_hist",
-             "select_pick", "select_tile_count", "select_scan", "select_mask", "compact_count",
+             "select_pick", "select_fixup", "select_scan", "select_mask", "compact_count",
              "compact_scan", "compact_scatter"]
     kern = {}
     for nm in names:
@@ -211,10 +211,11 @@ def main():
     hbm_bytes = {
         # gather K and V rows, write them packed, idx, read the mask
         "compact_scatter": K * (4 * row_bytes + 4) + N,
-        # reads of S: two radix-histogram passes, the tie count per tile (it
-        # runs when the K-th boundary splits a run of equal scores, as fp32
-        # maxima collide on these caches) and the mask pass; plus the mask write
-        "select_total": 4 * 4 * N + N,
+        # reads of S: two radix-histogram passes and the mask pass; plus the
+        # mask write.  When the K-th boundary splits a run of equal scores
+        # (fp32 maxima collide on these caches) the tie fix-up re-reads only
+        # the few tiles holding kept ties, which is left out
+        "select_total": 3 * 4 * N + N,
     }
     hbm = {}
     if "compact_scatter" in kern:
