@@ -208,6 +208,11 @@ __global__ __launch_bounds__(256) void score_pass1_bf16(
     }
   }
 
+  // a wave whose rows are all padding (only in the last row tile) still
+  // copies its share of every K tile and passes the barriers, but skips the
+  // MFMAs and exps, leaving its SIMD to the other resident waves
+  const bool live = rt * ROWS + wave * (32 * NQ) < R;
+
   float m[NQ], l[NQ];
 #pragma unroll
   for (int t = 0; t < NQ; ++t) {
@@ -280,6 +285,12 @@ __global__ __launch_bounds__(256) void score_pass1_bf16(
     // tile it occupied
     auto body = [&](int it, f32x16 (&cur)[NQ], f32x16 (&nxt)[NQ], int par) {
       const int buf = par ^ 1;
+      if (!live) {
+        copy_tile(min(it + 2, last), par);
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+        return;
+      }
       bf16x8 a[AW];
 #pragma unroll
       for (int ks = 0; ks < AW; ++ks)
@@ -358,6 +369,7 @@ __global__ __launch_bounds__(256) void score_pass1_bf16(
     load_tile(tile);
     store_tile(0);
     __syncthreads();
+    if (!live) continue;
     f32x16 c[NQ];
     mfma_tile(0, c);
     const int key0 = tile * KT;
@@ -420,7 +432,8 @@ __global__ __launch_bounds__(256) void score_combine(const float2* __restrict__ 
 // tile); every A operand read from LDS feeds NT MFMAs.  The epilogue of a key
 // tile (fma with the row lse and a running max, or the sum / raw variants)
 // overlaps the MFMAs of the following key tiles of the same query tile.
-// Padding rows (r >= R) re-read row R-1 and carry lse = +inf.
+// Padding rows (r >= R) of the last row tile read as zero queries and carry
+// lse = +inf (raw logits: a -inf accumulator start).
 // MODE: 0 = max of probabilities (the method), 1 = sum of probabilities,
 // 2 = max of raw logits scale * q . k (no softmax; lse2 unused)
 // ---------------------------------------------------------------------------
@@ -468,7 +481,8 @@ __global__ __launch_bounds__(256) void score_pass2_bf16(
   // one per lane, so each lane fetches the (row, chunk) that the swizzled
   // layout puts in its slot.  The buffer covers the R rows of head h: padding
   // rows (r >= R) fall outside it and read as zero (they carry lse = +inf).
-  const int n_tiles = R_pad / RT;
+  // row tiles holding real rows (the padding up to R_pad adds nothing)
+  const int n_tiles = (R + RT - 1) / RT;
   const uint16_t* qh = q + (size_t)h * R * D;
   const float* lseh = lse2 + (size_t)h * R_pad;
   int qoff[LOADS];
@@ -532,8 +546,14 @@ __global__ __launch_bounds__(256) void score_pass2_bf16(
       // accumulator start: -lse2/(scale log2 e) of the lane's 16 rows
 #pragma unroll
       for (int v = 0; v < 16; ++v) z[v] = L[v >> 2][v & 3];
+    } else if (MODE == 2) {
+      // raw logits: padding rows (r >= R, zero queries) start at -inf so
+      // that their zero logit never enters the max
+      const int r0 = it * RT + 4 * half;
+#pragma unroll
+      for (int v = 0; v < 16; ++v) z[v] = r0 + 8 * (v >> 2) + (v & 3) < R ? 0.f : -INFINITY;
     } else {
-      z = f32x16{};
+      z = f32x16{};  // sum: padding rows carry lse = +inf and add 0
     }
     __builtin_amdgcn_sched_barrier(0);
     // MFMAs of key tile t, each followed by a share of key tile t-1's epilogue

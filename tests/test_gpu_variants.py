@@ -79,6 +79,31 @@ def test_sum_and_raw_zero_query_closed_forms():
     assert np.all(R.cpu().numpy() == 0.0)
 
 
+@pytest.mark.parametrize("d,G,n_in", [(128, 1, 3), (64, 2, 7), (256, 1, 33)])
+def test_raw_logits_few_rows(d, G, n_in):
+    """Query rows that leave the last 32-row tile partly padding, and keys
+    that see only negative logits (positive queries, every third context key
+    negative): the raw maximum must come from real rows only (a zero-query
+    padding row would give 0)."""
+    H, n_c = 2, 700
+    rng = np.random.default_rng(26 + d + n_in)
+    kc32 = rng.standard_normal((H, n_c, d)).astype(np.float32)
+    kc32[:, ::3] = -np.abs(kc32[:, ::3])
+    kc = bf16_bits(kc32)
+    ki = bf16_bits(rng.standard_normal((H, n_in, d)).astype(np.float32))
+    q = bf16_bits(np.abs(rng.standard_normal((H, G, n_in, d))).astype(np.float32))
+    scale = 1 / math.sqrt(d)
+    S = torch.full((H, n_c), -np.inf, dtype=torch.float32, device="cuda")
+    kvz.kvz_score_chunk_ex(to_dev(q, "bf16"), to_dev(kc, "bf16"), to_dev(ki, "bf16"), S, 1, "raw",
+                           scale)
+    torch.cuda.synchronize()
+    ref = np.full((H, n_c), -np.inf)
+    ras.score_chunk(ras.to_f64(q, "bf16"), ras.to_f64(kc, "bf16"), ras.to_f64(ki, "bf16"), scale,
+                    ref, mode="raw")
+    assert (ref < 0).mean() > 0.3, "too few keys with only negative logits"
+    assert_scores_close(S.cpu().numpy(), ref, atol=1e-4, rtol=1e-4, what=f"raw d={d} R={G * n_in}")
+
+
 def test_select_over_signed_raw_scores():
     """Raw-logit scores are signed; selection must still be the exact top-K
     of the oracle on the same fp32 values (including -0.0 and ties)."""
