@@ -513,31 +513,33 @@ __global__ __launch_bounds__(TPB) void sel_fixup(const float* __restrict__ S,
   if (t == 0) keptc[tile] += added;
 }
 
-// one workgroup: head offsets from a scan of the per-tile kept counts (a
-// head's tiles are consecutive, so its offset is the prefix at its first
-// tile), the total, tau
+// one workgroup: per-head budgets (each thread sums the tile counts of its
+// heads) and their exclusive scan; tau
 __global__ __launch_bounds__(SCAN_T) void sel_heads(const SelState* __restrict__ st,
                                                     const uint32_t* __restrict__ keptc,
                                                     int64_t* __restrict__ head_offsets,
                                                     float* __restrict__ tau_out,
                                                     int tiles_per_head, int64_t n_heads) {
   __shared__ uint32_t buf[SCAN_W];
-  // this thread's next head start at or after the tile being written (one
-  // division per round: a thread's tiles are consecutive within a round)
-  int64_t hb = 0, nb = -1;
-  const long long total = scan_tiles(keptc, n_heads * tiles_per_head, buf,
-                                     [&](int64_t i, long long before) {
-                                       if (nb < i) {
-                                         hb = (i + tiles_per_head - 1) / tiles_per_head;
-                                         nb = hb * tiles_per_head;
-                                       }
-                                       if (i == nb) {
-                                         head_offsets[hb] = before;
-                                         ++hb;
-                                         nb += tiles_per_head;
-                                       }
-                                     });
-  if (threadIdx.x == 0) {
+  const int t = threadIdx.x;
+  const int64_t hper = (n_heads + SCAN_T - 1) / SCAN_T;
+  const int64_t h0 = (int64_t)t * hper, h1 = min(n_heads, h0 + hper);
+  auto head_sum = [&](int64_t h) {
+    const uint32_t* kp = keptc + h * tiles_per_head;
+    uint32_t s = 0;
+#pragma unroll 8
+    for (int k = 0; k < tiles_per_head; ++k) s += kp[k];
+    return s;
+  };
+  uint32_t hs = 0;
+  for (int64_t h = h0; h < h1; ++h) hs += head_sum(h);
+  uint32_t total;
+  long long hrun = block_exclusive_scan(hs, buf, &total);
+  for (int64_t h = h0; h < h1; ++h) {
+    head_offsets[h] = hrun;
+    hrun += head_sum(h);
+  }
+  if (t == 0) {
     head_offsets[n_heads] = total;
     *tau_out = key_to_float(st->tau);
   }
