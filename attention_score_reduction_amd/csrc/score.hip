@@ -26,6 +26,8 @@
 // fp32 path: plain VALU kernels for small fp32 problems.
 #include <math.h>
 
+#include <type_traits>
+
 #include "common.h"
 
 namespace kvz {
@@ -136,8 +138,9 @@ __device__ __forceinline__ int acc_row(int v, int half) {
 // NQ*KS MFMAs of tile t+1 into one accumulator set and, between them in a
 // fixed order, the exp/sum work of tile t from the other set; then it waits
 // for its copies and passes one barrier.  A operands are read AW k-steps
-// ahead.  The online sum is lazy (tile_sum).  Masked tiles (the ragged last
-// context tile, the causal chunk keys) take a simple unpipelined path.
+// ahead.  The online sum is lazy (tile_sum).  The causal chunk keys run the
+// same loop with the mask in the accumulator start; the ragged last context
+// tile takes a simple unpipelined path.
 // ---------------------------------------------------------------------------
 template <int D>
 struct P1Shape {
@@ -186,7 +189,7 @@ __global__ __launch_bounds__(256) void score_pass1_bf16(
     const int rlast = min(R, (rt + 1) * ROWS) - 1;
     t_begin = 0;
     t_end = (rlast / G) / KT + 1;
-    t_clean = t_begin;  // every in-chunk tile is causally masked
+    t_clean = t_end;  // pipelined, causal mask in the accumulator start
   }
 
   // stationary query operand (B of K*Q^T): this lane's query column n of
@@ -274,96 +277,129 @@ __global__ __launch_bounds__(256) void score_pass1_bf16(
       for (int u = 0; u < LOADS; ++u)
         copy16_to_lds(kseg, seg_bytes, koff[u] + rt_ * (KT * D * 2), ldsb(buf) + (u * 4 + wave) * 64);
     };
-    copy_tile(0, 0);
-    copy_tile(min(1, last), 1);
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-    mfma_tile(0, A);
-    __syncthreads();  // every wave has read buffer 0 before it is refilled
-    // iteration it (parity par = it & 1, a literal at each call): MFMAs of
-    // tile it+1, exp/sum work of tile it, copy of tile it+2 into the buffer
-    // tile it occupied
-    auto body = [&](int it, f32x16 (&cur)[NQ], f32x16 (&nxt)[NQ], int par) {
-      const int buf = par ^ 1;
-      if (!live) {
-        copy_tile(min(it + 2, last), par);
-        __builtin_amdgcn_s_waitcnt(0);
-        __syncthreads();
-        return;
-      }
-      bf16x8 a[AW];
+    // The causal in-chunk split runs the same loop with its mask in the
+    // accumulator start: for query tile t, the MFMA over the first k-step
+    // of a key tile starts at 0 on the keys its row sees and -inf on the
+    // keys past it, so every logit consumer (exp/sum, lazy commit, exact
+    // fallback) sees -inf there.  Instantiated twice (CAUSAL false/true) so
+    // the context splits keep their zero start.
+    auto run = [&](auto causal_c) {
+      constexpr bool CAUSAL = decltype(causal_c)::value;
+      auto mfma_first = [&](const bf16x8& a, const bf16x8& b, int tile, int t) -> f32x16 {
+        if constexpr (CAUSAL) {
+          // key row k of the tile is visible to this lane's row iff k <= lim
+          const int lim = irow[t] - tile * KT - 4 * half;
+          f32x16 zz;
 #pragma unroll
-      for (int ks = 0; ks < AW; ++ks)
-        a[ks] = as_bf16x8(ldsb(buf)[swz<CH, SWZ>(n, ks * 2 + half)]);
-      copy_tile(min(it + 2, last), par);
-      __builtin_amdgcn_sched_barrier(0);
-      const f32x16 z = {};
-      float sm[NQ][4], ex[NE];
-      // three-stage VALU pipeline over the chunks: the fma of a logit is
-      // issued one chunk (one MFMA) before its exp, and its add one chunk
-      // after, so no VALU op waits on the result of the op just before it
-      auto fma_chunk = [&](int c) {
-#pragma unroll
-        for (int e = chunk_lo<NE, NCH>(c); e < chunk_lo<NE, NCH>(c + 1); ++e) {
-          const int col = e >> 4, v = e & 15;
-          ex[e] = fmaf(cur[col][v], cl2, -m[col]);
+          for (int v = 0; v < 16; ++v) zz[v] = 8 * (v >> 2) + (v & 3) > lim ? -INFINITY : 0.f;
+          return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, zz, 0, 0, 0);
+        } else {
+          const f32x16 z = {};
+          return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, z, 0, 0, 0);
         }
       };
-      auto exp_chunk = [&](int c) {
-#pragma unroll
-        for (int e = chunk_lo<NE, NCH>(c); e < chunk_lo<NE, NCH>(c + 1); ++e)
-          ex[e] = fast_exp2(ex[e]);
-      };
-      auto add_chunk = [&](int c) {
-#pragma unroll
-        for (int e = chunk_lo<NE, NCH>(c); e < chunk_lo<NE, NCH>(c + 1); ++e) {
-          const int col = e >> 4, v = e & 15;
-          if (v < 4) sm[col][v] = ex[e]; else sm[col][v & 3] += ex[e];
-        }
-      };
-      fma_chunk(0);
-#pragma unroll
-      for (int c = 0; c < NCH; ++c) {
-        // logits [chunk_lo(c), chunk_lo(c+1)) of this lane's 16*NQ
-        exp_chunk(c);
-        if (c + 1 < NCH) fma_chunk(c + 1);
-        if (c > 0) add_chunk(c - 1);
-        __builtin_amdgcn_sched_barrier(0);
-        const int ks = c / NQ, t = c % NQ;
-        nxt[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[ks % AW], qr[t][ks],
-                                                         ks == 0 ? z : nxt[t], 0, 0, 0);
-        if (t == NQ - 1 && ks + AW < KS)
-          a[ks % AW] = as_bf16x8(ldsb(buf)[swz<CH, SWZ>(n, (ks + AW) * 2 + half)]);
-        __builtin_amdgcn_sched_barrier(0);
-      }
-      add_chunk(NCH - 1);
-      float tot[NQ];
-#pragma unroll
-      for (int t = 0; t < NQ; ++t) tot[t] = (sm[t][0] + sm[t][1]) + (sm[t][2] + sm[t][3]);
-      lazy_commit<NQ>(cur, tot, m, l, cl2);
-      __builtin_amdgcn_s_waitcnt(0);  // this wave's copy of tile it+2 has landed
+      copy_tile(0, 0);
+      copy_tile(min(1, last), 1);
+      __builtin_amdgcn_s_waitcnt(0);
       __syncthreads();
-    };
-    auto finish = [&](f32x16 (&cur)[NQ]) {
-      float tot[NQ];
 #pragma unroll
-      for (int t = 0; t < NQ; ++t) tot[t] = tile_sum(cur[t], m[t], cl2);
-      lazy_commit<NQ>(cur, tot, m, l, cl2);
+      for (int ks = 0; ks < KS; ++ks) {
+        const bf16x8 a = as_bf16x8(ldsb(0)[swz<CH, SWZ>(n, ks * 2 + half)]);
+#pragma unroll
+        for (int t = 0; t < NQ; ++t)
+          A[t] = ks == 0 ? mfma_first(a, qr[t][0], t_begin, t)
+                         : __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qr[t][ks], A[t], 0, 0, 0);
+      }
+      __syncthreads();  // every wave has read buffer 0 before it is refilled
+      // iteration it (parity par = it & 1, a literal at each call): MFMAs of
+      // tile it+1, exp/sum work of tile it, copy of tile it+2 into the buffer
+      // tile it occupied
+      auto body = [&](int it, f32x16 (&cur)[NQ], f32x16 (&nxt)[NQ], int par) {
+        const int buf = par ^ 1;
+        if (!live) {
+          copy_tile(min(it + 2, last), par);
+          __builtin_amdgcn_s_waitcnt(0);
+          __syncthreads();
+          return;
+        }
+        bf16x8 a[AW];
+#pragma unroll
+        for (int ks = 0; ks < AW; ++ks)
+          a[ks] = as_bf16x8(ldsb(buf)[swz<CH, SWZ>(n, ks * 2 + half)]);
+        copy_tile(min(it + 2, last), par);
+        __builtin_amdgcn_sched_barrier(0);
+        float sm[NQ][4], ex[NE];
+        // three-stage VALU pipeline over the chunks: the fma of a logit is
+        // issued one chunk (one MFMA) before its exp, and its add one chunk
+        // after, so no VALU op waits on the result of the op just before it
+        auto fma_chunk = [&](int c) {
+#pragma unroll
+          for (int e = chunk_lo<NE, NCH>(c); e < chunk_lo<NE, NCH>(c + 1); ++e) {
+            const int col = e >> 4, v = e & 15;
+            ex[e] = fmaf(cur[col][v], cl2, -m[col]);
+          }
+        };
+        auto exp_chunk = [&](int c) {
+#pragma unroll
+          for (int e = chunk_lo<NE, NCH>(c); e < chunk_lo<NE, NCH>(c + 1); ++e)
+            ex[e] = fast_exp2(ex[e]);
+        };
+        auto add_chunk = [&](int c) {
+#pragma unroll
+          for (int e = chunk_lo<NE, NCH>(c); e < chunk_lo<NE, NCH>(c + 1); ++e) {
+            const int col = e >> 4, v = e & 15;
+            if (v < 4) sm[col][v] = ex[e]; else sm[col][v & 3] += ex[e];
+          }
+        };
+        fma_chunk(0);
+#pragma unroll
+        for (int c = 0; c < NCH; ++c) {
+          // logits [chunk_lo(c), chunk_lo(c+1)) of this lane's 16*NQ
+          exp_chunk(c);
+          if (c + 1 < NCH) fma_chunk(c + 1);
+          if (c > 0) add_chunk(c - 1);
+          __builtin_amdgcn_sched_barrier(0);
+          const int ks = c / NQ, t = c % NQ;
+          nxt[t] = ks == 0 ? mfma_first(a[0], qr[t][0], t_begin + it + 1, t)
+                           : __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[ks % AW], qr[t][ks], nxt[t],
+                                                                     0, 0, 0);
+          if (t == NQ - 1 && ks + AW < KS)
+            a[ks % AW] = as_bf16x8(ldsb(buf)[swz<CH, SWZ>(n, (ks + AW) * 2 + half)]);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        add_chunk(NCH - 1);
+        float tot[NQ];
+#pragma unroll
+        for (int t = 0; t < NQ; ++t) tot[t] = (sm[t][0] + sm[t][1]) + (sm[t][2] + sm[t][3]);
+        lazy_commit<NQ>(cur, tot, m, l, cl2);
+        __builtin_amdgcn_s_waitcnt(0);  // this wave's copy of tile it+2 has landed
+        __syncthreads();
+      };
+      auto finish = [&](f32x16 (&cur)[NQ]) {
+        float tot[NQ];
+#pragma unroll
+        for (int t = 0; t < NQ; ++t) tot[t] = tile_sum(cur[t], m[t], cl2);
+        lazy_commit<NQ>(cur, tot, m, l, cl2);
+      };
+      int it = 0;
+      for (; it + 2 < nclean; it += 2) {
+        body(it, A, B, 0);
+        body(it + 1, B, A, 1);
+      }
+      if (it + 1 < nclean) {
+        body(it, A, B, 0);
+        finish(B);
+      } else {
+        finish(A);
+      }
     };
-    int it = 0;
-    for (; it + 2 < nclean; it += 2) {
-      body(it, A, B, 0);
-      body(it + 1, B, A, 1);
-    }
-    if (it + 1 < nclean) {
-      body(it, A, B, 0);
-      finish(B);
-    } else {
-      finish(A);
-    }
+    if (inchunk)
+      run(std::true_type{});
+    else
+      run(std::false_type{});
   }
 
-  // masked tiles: ragged context tail or causal in-chunk keys
+  // masked tiles: the ragged context tail
   for (int tile = t_clean; tile < t_end; ++tile) {
     __syncthreads();
     load_tile(tile);
@@ -378,7 +414,7 @@ __global__ __launch_bounds__(256) void score_pass1_bf16(
       const int key = key0 + acc_row(v, half);
 #pragma unroll
       for (int t = 0; t < NQ; ++t)
-        if (inchunk ? key > irow[t] : key >= n_c) c[t][v] = -INFINITY;
+        if (key >= n_c) c[t][v] = -INFINITY;
     }
 #pragma unroll
     for (int t = 0; t < NQ; ++t) online_update(c[t], m[t], l[t], cl2);
