@@ -186,25 +186,47 @@ __global__ __launch_bounds__(TPB) void decode_split(const T* __restrict__ q,
   }
 }
 
-// one workgroup per (head, g): merge the head's valid segments
+// one workgroup per (head, g): merge the head's valid segments.  The max is
+// a strided reduction over the segments; the weighted sums take the
+// segments eight at a time so that their loads are in flight together.
 template <int D>
 __global__ __launch_bounds__(D) void decode_combine(const float* __restrict__ part,
                                                      const int64_t* __restrict__ offs,
                                                      float* __restrict__ out, int G, int n_seg,
                                                      int seg_rows) {
+  constexpr int NWV = D / 64;  // waves per workgroup
+  constexpr int U = 8;         // segments per batch
+  __shared__ float red[NWV];
   const int64_t h = blockIdx.x / G;
   const int g = blockIdx.x - (int)h * G;
   const int dd = threadIdx.x;
   const int64_t len = offs[h + 1] - offs[h];
   const int nv = (int)min((int64_t)n_seg, (len + seg_rows - 1) / seg_rows);
   float M = kNeg;
-  for (int s = 0; s < nv; ++s) M = fmaxf(M, part[part_off<D>(h, s, n_seg, g, G)]);
+  for (int s = dd; s < nv; s += D) M = fmaxf(M, part[part_off<D>(h, s, n_seg, g, G)]);
+  for (int off = 32; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
+  if ((dd & 63) == 0) red[dd >> 6] = M;
+  __syncthreads();
+  M = red[0];
+#pragma unroll
+  for (int w = 1; w < NWV; ++w) M = fmaxf(M, red[w]);
   float L = 0.f, A = 0.f;
-  for (int s = 0; s < nv; ++s) {
-    const float* pp = part + part_off<D>(h, s, n_seg, g, G);
-    const float f = exp2f(pp[0] - M);
-    L += pp[1] * f;
-    A += pp[2 + dd] * f;
+  for (int s0 = 0; s0 < nv; s0 += U) {
+    float m[U], l[U], a[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const bool ok = s0 + u < nv;
+      const float* pp = part + part_off<D>(h, ok ? s0 + u : 0, n_seg, g, G);
+      m[u] = ok ? pp[0] : kNeg;
+      l[u] = ok ? pp[1] : 0.f;
+      a[u] = ok ? pp[2 + dd] : 0.f;
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const float f = exp2f(m[u] - M);
+      L += l[u] * f;
+      A += a[u] * f;
+    }
   }
   out[(h * G + g) * D + dd] = nv > 0 ? A / L : 0.f;
 }
