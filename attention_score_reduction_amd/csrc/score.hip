@@ -449,9 +449,12 @@ __global__ __launch_bounds__(256) void score_combine(const float2* __restrict__ 
     return;
   }
   const float2* p = part + (size_t)h * splits * R_pad + r;
+  // unrolled so that the split loads are in flight together
   float M = kNegBig;
+#pragma unroll 8
   for (int s = 0; s < splits; ++s) M = fmaxf(M, p[(size_t)s * R_pad].x);
   float L = 0.f;
+#pragma unroll 8
   for (int s = 0; s < splits; ++s) {
     const float2 v = p[(size_t)s * R_pad];
     L += v.y * exp2f(v.x - M);
