@@ -131,7 +131,7 @@ __device__ __forceinline__ int acc_row(int v, int half) {
 //
 // Each wave keeps NQ 32-row query tiles in registers (the B operand of
 // K*Q^T) and sweeps 32-key tiles of K staged in LDS; every A operand read
-// from LDS feeds NQ MFMAs.  Main loop (tiles with no masked key),
+// from LDS feeds NQ MFMAs.  Main loop (every tile but a ragged last one),
 // software-pipelined: iteration t reads its first A operands of tile t+1,
 // starts the global -> LDS copy of tile t+2 into the buffer tile t occupied
 // (buffer loads with an LDS destination: no register staging), issues the
