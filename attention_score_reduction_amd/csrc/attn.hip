@@ -379,7 +379,7 @@ hipError_t launch3(kvz_dtype dt, const ScorePlan& p, const AttnPlan& a, const vo
 AttnPlan attn_plan(kvz_dtype dt, const ScorePlan& p) {
   AttnPlan a{};
   if (dt != KVZ_BF16) return a;  // the fp32 kernel needs no workspace of its own
-  a.n_rt = p.R_pad / ROWS3;
+  a.n_rt = (p.R + ROWS3 - 1) / ROWS3;  // row tiles holding real rows (<= R_pad / ROWS3)
   const int n_ctx_tiles = (p.n_c + KT - 1) / KT;
   int want = (KVZ_ATTN_TARGET_WGS + p.H * a.n_rt - 1) / (p.H * a.n_rt);
   int maxs = n_ctx_tiles / 16;
