@@ -14,12 +14,12 @@
 // Passes over S (N floats): three, plus a re-read of the few tiles whose
 // ties are kept when the K-th boundary splits a run of equal scores.
 //   sel_init       zero the histograms and the search state
-//   sel_hist0      full read: histogram of bits 31..21 (2048 bins)
+//   sel_hist0      full read: histogram of bits 31..20 (4096 bins)
 //   sel_pick<0>    the top-level bin b0 holding the K-th largest
 //   sel_hist12     full read: for scores in bin b0, a histogram of bits
-//                  20..10 (2048 bins) and a joint histogram of bits 20..0
-//                  (2M bins, global memory)
-//   sel_pick<1>    bin b1 of bits 20..10
+//                  19..10 (1024 bins) and a joint histogram of bits 19..0
+//                  (1M bins, global memory)
+//   sel_pick<1>    bin b1 of bits 19..10
 //   sel_pick2      bin b2 of bits 9..0 from the joint histogram row b1:
 //                  tau, the number of ties to keep, and whether every
 //                  score equal to tau is kept (the common case for
@@ -39,8 +39,11 @@ namespace kvz {
 
 namespace {
 
-constexpr int BINS = 2048;
-constexpr int JBINS = 1 << 21;    // joint histogram of bits 20..0
+// radix digits of the 32-bit key: bits 31..20 (first pass), 19..10 and 9..0
+constexpr int B0_SHIFT = 20;
+constexpr int BINS0 = 1 << (32 - B0_SHIFT);  // 4096
+constexpr int BINS1 = 1024;                  // bits 19..10
+constexpr int JBINS = 1 << B0_SHIFT;         // joint histogram of bits 19..0
 constexpr int TILE = 4096;        // scores per mask tile (within one head)
 constexpr int TPB = 256;          // threads per block
 constexpr int PER_T = TILE / TPB; // 16 scores per thread per tile
@@ -70,7 +73,7 @@ __global__ void sel_init(uint32_t* __restrict__ hist, uint32_t* __restrict__ joi
                          SelState* __restrict__ st, long long K) {
   const int t = blockIdx.x * blockDim.x + threadIdx.x;
   const int stride = gridDim.x * blockDim.x;
-  for (int i = t; i < 2 * BINS; i += stride) hist[i] = 0;
+  for (int i = t; i < BINS0 + BINS1; i += stride) hist[i] = 0;
   for (int i = t; i < JBINS; i += stride) joint[i] = 0;
   if (t == 0) {
     st->b0 = st->b1 = st->tau = st->split_ties = 0;
@@ -85,8 +88,8 @@ __global__ __launch_bounds__(TPB) void sel_hist0(const float* __restrict__ S, lo
   // HR copies of every bin in consecutive banks, copy = lane % HR: lanes of
   // a wave that hit the same bin (scores crowd into few bins) spread over HR
   // banks instead of serialising on one
-  __shared__ uint32_t h[BINS * HR];
-  for (int b = threadIdx.x; b < BINS * HR; b += TPB) h[b] = 0;
+  __shared__ uint32_t h[BINS0 * HR];
+  for (int b = threadIdx.x; b < BINS0 * HR; b += TPB) h[b] = 0;
   __syncthreads();
   const uint32_t rep = threadIdx.x & (HR - 1);
   const long long n4 = N >> 2;
@@ -103,18 +106,18 @@ __global__ __launch_bounds__(TPB) void sel_hist0(const float* __restrict__ S, lo
 #pragma unroll
     for (int u = 0; u < HU; ++u) {
       if (i0 + (long long)u * TPB < n4) {
-        atomicAdd(&h[(fkey(v[u].x) >> 21) * HR + rep], 1u);
-        atomicAdd(&h[(fkey(v[u].y) >> 21) * HR + rep], 1u);
-        atomicAdd(&h[(fkey(v[u].z) >> 21) * HR + rep], 1u);
-        atomicAdd(&h[(fkey(v[u].w) >> 21) * HR + rep], 1u);
+        atomicAdd(&h[(fkey(v[u].x) >> B0_SHIFT) * HR + rep], 1u);
+        atomicAdd(&h[(fkey(v[u].y) >> B0_SHIFT) * HR + rep], 1u);
+        atomicAdd(&h[(fkey(v[u].z) >> B0_SHIFT) * HR + rep], 1u);
+        atomicAdd(&h[(fkey(v[u].w) >> B0_SHIFT) * HR + rep], 1u);
       }
     }
   }
   if (blockIdx.x == 0)
     for (long long i = (n4 << 2) + threadIdx.x; i < N; i += TPB)
-      atomicAdd(&h[(fkey(S[i]) >> 21) * HR + rep], 1u);
+      atomicAdd(&h[(fkey(S[i]) >> B0_SHIFT) * HR + rep], 1u);
   __syncthreads();
-  for (int b = threadIdx.x; b < BINS; b += TPB) {
+  for (int b = threadIdx.x; b < BINS0; b += TPB) {
     uint32_t c = 0;
 #pragma unroll
     for (int r = 0; r < HR; ++r) c += h[b * HR + r];
@@ -128,14 +131,14 @@ __global__ __launch_bounds__(TPB) void sel_hist12(const float* __restrict__ S, l
                                                   uint32_t* __restrict__ hist1,
                                                   uint32_t* __restrict__ joint,
                                                   const SelState* __restrict__ st) {
-  __shared__ uint32_t h[BINS * HR];  // lane-replicated, as in sel_hist0
-  for (int b = threadIdx.x; b < BINS * HR; b += TPB) h[b] = 0;
+  __shared__ uint32_t h[BINS1 * HR];  // lane-replicated, as in sel_hist0
+  for (int b = threadIdx.x; b < BINS1 * HR; b += TPB) h[b] = 0;
   __syncthreads();
   const uint32_t b0 = st->b0;
   const uint32_t rep = threadIdx.x & (HR - 1);
   auto add = [&](uint32_t k) {
-    if ((k >> 21) == b0) {
-      atomicAdd(&h[((k >> 10) & 0x7FF) * HR + rep], 1u);
+    if ((k >> B0_SHIFT) == b0) {
+      atomicAdd(&h[((k >> 10) & (BINS1 - 1)) * HR + rep], 1u);
       atomicAdd(&joint[k & (JBINS - 1)], 1u);
     }
   };
@@ -162,7 +165,7 @@ __global__ __launch_bounds__(TPB) void sel_hist12(const float* __restrict__ S, l
   if (blockIdx.x == 0)
     for (long long i = (n4 << 2) + threadIdx.x; i < N; i += TPB) add(fkey(S[i]));
   __syncthreads();
-  for (int b = threadIdx.x; b < BINS; b += TPB) {
+  for (int b = threadIdx.x; b < BINS1; b += TPB) {
     uint32_t c = 0;
 #pragma unroll
     for (int r = 0; r < HR; ++r) c += h[b * HR + r];
@@ -216,7 +219,10 @@ __global__ __launch_bounds__(TPB) void sel_pick(const uint32_t* __restrict__ his
   if (threadIdx.x == 0) d = -1;
   __syncthreads();
   const long long krem = st->krem[ROUND];
-  suffix_pick<BINS>(hist + ROUND * BINS, krem, part, &d, &above);
+  if (ROUND == 0)
+    suffix_pick<BINS0>(hist, krem, part, &d, &above);
+  else
+    suffix_pick<BINS1>(hist + BINS0, krem, part, &d, &above);
   __syncthreads();
   if (threadIdx.x == 0 && d >= 0) {
     if (ROUND == 0) st->b0 = (uint32_t)d; else st->b1 = (uint32_t)d;
@@ -238,7 +244,7 @@ __global__ __launch_bounds__(TPB) void sel_pick2(const uint32_t* __restrict__ jo
   __syncthreads();
   if (threadIdx.x == 0 && d >= 0) {
     const long long need = krem - above;  // ties to keep
-    st->tau = (st->b0 << 21) | (st->b1 << 10) | (uint32_t)d;
+    st->tau = (st->b0 << B0_SHIFT) | (st->b1 << 10) | (uint32_t)d;
     st->krem[3] = need;
     st->split_ties = need < (long long)row[d] ? 1u : 0u;
   }
@@ -557,7 +563,7 @@ __global__ void sel_empty(uint8_t* mask, long long N, int64_t* head_offsets, int
 }
 
 struct SelWs {
-  uint32_t* hist;      // [2][BINS]
+  uint32_t* hist;      // [BINS0 + BINS1]
   uint32_t* joint;     // [JBINS]
   SelState* st;
   uint32_t* eqc;       // [n_tiles]
@@ -569,7 +575,7 @@ SelWs carve(const SelectPlan& p, void* ws) {
   char* w = reinterpret_cast<char*>(ws);
   SelWs s;
   s.hist = reinterpret_cast<uint32_t*>(w);
-  w += align256(2 * BINS * sizeof(uint32_t));
+  w += align256((BINS0 + BINS1) * sizeof(uint32_t));
   s.joint = reinterpret_cast<uint32_t*>(w);
   w += align256(JBINS * sizeof(uint32_t));
   s.st = reinterpret_cast<SelState*>(w);
@@ -591,7 +597,7 @@ SelectPlan select_plan(int64_t n_heads, int n_c) {
   p.N = n_heads * (int64_t)n_c;
   p.tiles_per_head = (n_c + TILE - 1) / TILE;
   p.n_tiles = n_heads * p.tiles_per_head;
-  p.total_bytes = align256(2 * BINS * sizeof(uint32_t)) + align256(JBINS * sizeof(uint32_t)) +
+  p.total_bytes = align256((BINS0 + BINS1) * sizeof(uint32_t)) + align256(JBINS * sizeof(uint32_t)) +
                   align256(sizeof(SelState)) + 2 * align256((size_t)p.n_tiles * sizeof(uint32_t)) +
                   align256((size_t)p.n_tiles * sizeof(long long));
   return p;
@@ -616,7 +622,7 @@ hipError_t select_launch(const SelectPlan& p, const float* S, int64_t K, uint8_t
   if (hb > 2048) hb = 2048;
   KVZ_LAUNCH("select_hist", sel_hist0, hb, TPB, 0, stream, S, (long long)p.N, w.hist);
   KVZ_LAUNCH("select_pick", sel_pick<0>, 1, TPB, 0, stream, w.hist, w.st);
-  KVZ_LAUNCH("select_hist", sel_hist12, hb, TPB, 0, stream, S, (long long)p.N, w.hist + BINS,
+  KVZ_LAUNCH("select_hist", sel_hist12, hb, TPB, 0, stream, S, (long long)p.N, w.hist + BINS0,
              w.joint, w.st);
   KVZ_LAUNCH("select_pick", sel_pick<1>, 1, TPB, 0, stream, w.hist, w.st);
   KVZ_LAUNCH("select_pick", sel_pick2, 1, TPB, 0, stream, w.joint, w.st);
