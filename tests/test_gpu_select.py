@@ -45,6 +45,19 @@ def test_select_random_and_ties(shape):
                 check_select(S, K)
 
 
+@pytest.mark.parametrize("shape", [(9000, 5), (8500, 8), (3000, 4097)])
+def test_select_many_tiles_and_heads(shape):
+    """More than 8192 score tiles (the tile scans take several rounds) and
+    more than 1024 heads (several heads per thread in the head-offset scan),
+    with runs of equal scores so that the K-th boundary splits ties."""
+    rng = np.random.default_rng(shape[0] + shape[1])
+    n_heads, n_c = shape
+    N = n_heads * n_c
+    S = (rng.integers(0, 7, shape) / 32).astype(np.float32)
+    for K in (1, N // 5, N // 2 + 3, N - 2):
+        check_select(S, K)
+
+
 def test_select_all_equal_and_zeros():
     S = np.zeros((6, 5000), np.float32)
     check_select(S, 12345)
