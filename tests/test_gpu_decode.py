@@ -42,6 +42,15 @@ def test_decode_variable_lengths(d, G):
     assert_scores_close(got, ref, atol=1e-4, rtol=1e-3, what=f"decode d={d} G={G}")
 
 
+@pytest.mark.parametrize("d,G", [(128, 4), (64, 2), (256, 1)])
+def test_decode_long_heads(d, G):
+    """Heads of up to 20 segments of 1024 rows: the segment merge takes
+    several batches of eight, including a partial last batch."""
+    lens = [8191, 8192, 8193, 20000, 3, 16385]
+    got, ref = _case(len(lens), G, d, lens, "bf16", 7 * d + G)
+    assert_scores_close(got, ref, atol=1e-4, rtol=1e-3, what=f"decode long d={d} G={G}")
+
+
 def test_decode_fp32_and_dense_baseline():
     got, ref = _case(3, 4, 64, [700, 0, 2500], "f32", 5)
     assert_scores_close(got, ref, atol=1e-4, rtol=1e-3, what="decode fp32")
