@@ -1,4 +1,11 @@
-"""Build libkvz.so for gfx950 with hipcc, in-tree (next to this file)."""
+"""Build libkvz.so for gfx950 with hipcc, in-tree (next to this file).
+
+The library carries a build id: the sha256 of its sources, the public header
+and the compiler flags (source_digest()).  The Python binding refuses to load
+a libkvz.so whose id differs from the digest of the files next to it, so a
+stale binary can never stand in for the checked-out source.
+"""
+import hashlib
 import os
 import subprocess
 import sys
@@ -23,17 +30,61 @@ FLAGS = [
 ]
 
 
+INCLUDE = os.path.normpath(os.path.join(HERE, "..", "include"))
+
+
+def source_digest() -> str:
+    """sha256 over every source file of the library (csrc/*.hip, csrc/*.h,
+    include/*.h, by relative path and content) and the compiler flags."""
+    h = hashlib.sha256()
+    files = []
+    for d, rel in ((CSRC, "csrc"), (INCLUDE, "include")):
+        for f in sorted(os.listdir(d)):
+            if f.endswith((".hip", ".h")):
+                files.append((f"{rel}/{f}", os.path.join(d, f)))
+    for rel, path in files:
+        h.update(rel.encode() + b"\0")
+        with open(path, "rb") as fh:
+            h.update(fh.read())
+        h.update(b"\0")
+    h.update(" ".join(FLAGS + SOURCES).encode())
+    return h.hexdigest()
+
+
 def build(verbose: bool = False) -> str:
+    """Compile every source to an object (in parallel), then link libkvz.so."""
     hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
-    srcs = [os.path.join(CSRC, s) for s in SOURCES]
+    objdir = os.path.join(HERE, "..", "_build")
+    os.makedirs(objdir, exist_ok=True)
+    bid = source_digest()
+    compile_flags = [f for f in FLAGS if f != "-shared"]
+    procs = []
+    objs = []
+    for src in SOURCES:
+        obj = os.path.join(objdir, src.replace(".hip", ".o"))
+        objs.append(obj)
+        cmd = ([hipcc] + compile_flags + [f'-DKVZ_BUILD_ID="{bid}"', "-I", INCLUDE, "-c",
+                                          os.path.join(CSRC, src), "-o", obj])
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        procs.append((src, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT,
+                                            text=True)))
+    failed = []
+    for src, p in procs:
+        out, _ = p.communicate()
+        if p.returncode != 0:
+            sys.stderr.write(out)
+            failed.append(src)
+    if failed:
+        raise RuntimeError(f"hipcc failed compiling {failed}")
     tmp = LIB + ".tmp"
-    cmd = [hipcc] + FLAGS + ["-I", os.path.join(HERE, "..", "include")] + srcs + ["-o", tmp]
+    cmd = [hipcc, "--offload-arch=gfx950", "-shared", "-fPIC"] + objs + ["-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         sys.stderr.write(r.stdout + r.stderr)
-        raise RuntimeError("hipcc failed building libkvz.so")
+        raise RuntimeError("hipcc failed linking libkvz.so")
     os.replace(tmp, LIB)
     return LIB
 

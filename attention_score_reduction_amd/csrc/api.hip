@@ -68,7 +68,13 @@ hipError_t clear_error() { return hipGetLastError(); }
 
 }  // namespace
 
+#ifndef KVZ_BUILD_ID
+#define KVZ_BUILD_ID "unknown"
+#endif
+
 extern "C" {
+
+const char* kvz_build_id(void) { return KVZ_BUILD_ID; }
 
 const char* kvz_status_string(kvz_status s) {
   switch (s) {

@@ -20,7 +20,7 @@ AGG = {"max": KVZ_AGG_MAX, "sum": KVZ_AGG_SUM, "raw": KVZ_AGG_RAW_MAX}
 
 # every symbol declared in include/kvz.h
 SYMBOLS = (
-    "kvz_status_string", "kvz_score_chunk_workspace", "kvz_score_chunk", "kvz_score_chunk_ex",
+    "kvz_build_id", "kvz_status_string", "kvz_score_chunk_workspace", "kvz_score_chunk", "kvz_score_chunk_ex",
     "kvz_score_chunk_attn_workspace", "kvz_score_chunk_attn",
     "kvz_keep_count", "kvz_select_workspace", "kvz_select_threshold", "kvz_compact_workspace",
     "kvz_compact", "kvz_head_scores", "kvz_token_scores", "kvz_decode_workspace",
@@ -46,6 +46,15 @@ def lib():
             f"{LIB_PATH} is missing: build it with `python -c 'import __graft_entry__ as g; g.build()'`"
             " (the HIP library is required; there is no CPU fallback)")
     L = ctypes.CDLL(LIB_PATH)
+    L.kvz_build_id.argtypes = []
+    L.kvz_build_id.restype = ctypes.c_char_p
+    from .build import source_digest
+    built, want = L.kvz_build_id().decode(), source_digest()
+    if built != want:
+        raise RuntimeError(
+            f"{LIB_PATH} was built from other sources (build id {built[:16]}) than the ones in "
+            f"this checkout (digest {want[:16]}): rebuild it with "
+            "`python -c 'import __graft_entry__ as g; g.build()'`")
     c_int, c_i64, c_sz, c_f, c_d, c_p = (ctypes.c_int, ctypes.c_int64, ctypes.c_size_t,
                                          ctypes.c_float, ctypes.c_double, ctypes.c_void_p)
     L.kvz_status_string.argtypes = [c_int]
@@ -119,10 +128,32 @@ def _ptr(t, name):
     return ctypes.c_void_p(t.data_ptr())
 
 
+def _need(t, name, dtype, numel=None, shape=None, device=None):
+    """Reject a tensor of the wrong dtype, size or device before any launch:
+    the kernels index raw pointers and would run past a short allocation."""
+    import torch
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if numel is not None and t.numel() < numel:
+        raise ValueError(f"{name} holds {t.numel()} elements, needs at least {numel}")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+
+
 def _ws(nbytes, device):
     import torch
     # uint8 storage; the caching allocator returns >= 256-byte aligned blocks
     return torch.empty(max(int(nbytes), 256), dtype=torch.uint8, device=device)
+
+
+def kvz_build_id() -> str:
+    """sha256 of the sources the loaded library was built from (it equals the
+    checkout's digest, or lib() refuses to load)."""
+    return lib().kvz_build_id().decode()
 
 
 def kvz_status_string(status: int) -> str:
@@ -217,9 +248,13 @@ def kvz_score_chunk_attn(q, k_ctx, k_in, v_ctx, v_in, S, n_prompt, O=None, scale
 def kvz_head_scores(S, out=None, stream=None):
     """[n_heads][n_c] fp32 -> [n_heads]: max over each head's tokens."""
     import torch
+    _need(S, "S", torch.float32)
+    if S.dim() != 2:
+        raise ValueError("S must be [n_heads][n_c]")
     n_heads, n_c = S.shape
     if out is None:
         out = torch.empty(n_heads, dtype=torch.float32, device=S.device)
+    _need(out, "out", torch.float32, numel=n_heads, device=S.device)
     _check(lib().kvz_head_scores(_ptr(S, "S"), n_heads, n_c, _ptr(out, "out"), _stream(stream)),
            "kvz_head_scores")
     return out
@@ -228,9 +263,13 @@ def kvz_head_scores(S, out=None, stream=None):
 def kvz_token_scores(S, out=None, stream=None):
     """[n_heads][n_c] fp32 -> [n_c]: max over all heads per token."""
     import torch
+    _need(S, "S", torch.float32)
+    if S.dim() != 2:
+        raise ValueError("S must be [n_heads][n_c]")
     n_heads, n_c = S.shape
     if out is None:
         out = torch.empty(n_c, dtype=torch.float32, device=S.device)
+    _need(out, "out", torch.float32, numel=n_c, device=S.device)
     _check(lib().kvz_token_scores(_ptr(S, "S"), n_heads, n_c, _ptr(out, "out"), _stream(stream)),
            "kvz_token_scores")
     return out
@@ -240,6 +279,9 @@ def kvz_select_threshold(S, K, mask=None, head_offsets=None, tau=None, ws=None, 
     """Exact top-K over S [n_heads][n_c] (fp32).  Returns (mask uint8 [N],
     head_offsets int64 [n_heads + 1], tau fp32 [1]), all on the device."""
     import torch
+    _need(S, "S", torch.float32)
+    if S.dim() != 2:
+        raise ValueError("S must be [n_heads][n_c]")
     n_heads, n_c = S.shape
     dev = S.device
     if mask is None:
@@ -248,8 +290,12 @@ def kvz_select_threshold(S, K, mask=None, head_offsets=None, tau=None, ws=None, 
         head_offsets = torch.empty(n_heads + 1, dtype=torch.int64, device=dev)
     if tau is None:
         tau = torch.empty(1, dtype=torch.float32, device=dev)
+    _need(mask, "mask", torch.uint8, numel=n_heads * n_c, device=dev)
+    _need(head_offsets, "head_offsets", torch.int64, numel=n_heads + 1, device=dev)
+    _need(tau, "tau", torch.float32, numel=1, device=dev)
     if ws is None:
         ws = _ws(kvz_select_workspace(n_heads, n_c), dev)
+    _need(ws, "ws", torch.uint8, device=dev)
     st = lib().kvz_select_threshold(_ptr(S, "S"), n_heads, n_c, int(K), _ptr(mask, "mask"),
                                     _ptr(head_offsets, "head_offsets"), _ptr(tau, "tau"),
                                     _ptr(ws, "ws"), ws.numel() * ws.element_size(),
@@ -262,12 +308,31 @@ def kvz_compact(k_ctx, v_ctx, mask, head_offsets, k_out, v_out, idx_out, head_be
                 ws=None, stream=None):
     """Pack heads [head_begin, head_begin + k_ctx.shape[0]) of the kept rows.
     k_ctx, v_ctx [head_count][n_c][d]; k_out, v_out [K][d]; idx_out int32 [K]."""
+    import torch
+    if k_ctx.dim() != 3:
+        raise ValueError("k_ctx must be [head_count][n_c][d]")
     head_count, n_c, d = k_ctx.shape
     dt = _dtype_code(k_ctx)
-    if v_ctx.shape != k_ctx.shape or v_ctx.dtype != k_ctx.dtype:
-        raise ValueError("k_ctx and v_ctx must match")
+    dev = k_ctx.device
+    _need(v_ctx, "v_ctx", k_ctx.dtype, shape=k_ctx.shape, device=dev)
+    end = int(head_begin) + head_count
+    if int(head_begin) < 0:
+        raise ValueError("head_begin must be >= 0")
+    _need(mask, "mask", torch.uint8, numel=end * n_c, device=dev)
+    _need(head_offsets, "head_offsets", torch.int64, numel=end + 1, device=dev)
+    # the packed outputs must hold every row up to the last head's offset;
+    # that offset lives on the device, so the check is on the row width and
+    # the caller sizes the row count from head_offsets
+    for t, nm in ((k_out, "k_out"), (v_out, "v_out")):
+        _need(t, nm, k_ctx.dtype, device=dev)
+        if t.dim() != 2 or t.shape[1] != d:
+            raise ValueError(f"{nm} must be [rows][{d}]")
+    _need(idx_out, "idx_out", torch.int32, device=dev)
+    if idx_out.dim() != 1 or idx_out.shape[0] != k_out.shape[0] or v_out.shape[0] != k_out.shape[0]:
+        raise ValueError("k_out, v_out and idx_out must hold the same number of rows")
     if ws is None:
-        ws = _ws(kvz_compact_workspace(head_count, n_c), k_ctx.device)
+        ws = _ws(kvz_compact_workspace(head_count, n_c), dev)
+    _need(ws, "ws", torch.uint8, device=dev)
     st = lib().kvz_compact(dt, d, n_c, int(head_begin), head_count, _ptr(k_ctx, "k_ctx"),
                            _ptr(v_ctx, "v_ctx"), _ptr(mask, "mask"),
                            _ptr(head_offsets, "head_offsets"), _ptr(k_out, "k_out"),

@@ -77,6 +77,12 @@ typedef enum {
 /* Human-readable name of a status code (static string, never NULL). */
 KVZ_API const char* kvz_status_string(kvz_status s);
 
+/* Build id of this library: the sha256 (hex) of the sources, this header and
+ * the compiler flags it was built from, or "unknown" when built without one.
+ * Callers compare it with the digest of their checkout to refuse a stale
+ * binary.  Static string, never NULL. */
+KVZ_API const char* kvz_build_id(void);
+
 /* ------------------------------------------------------------------------
  * Scoring of one reconstruction chunk for all KV heads of one layer
  * (blog 4.3.1, 4.3.2, 4.5.1; rebuttal, positional OOD).

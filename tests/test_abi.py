@@ -197,3 +197,127 @@ def test_package_exports_every_binding():
     for n in kvz.SYMBOLS:
         if hasattr(kvz, n):
             assert hasattr(pkg, n), n
+
+
+# The Python bindings check dtypes, sizes and devices before any launch.  These
+# run on CPU tensors: each bad argument is caught by a check that comes before
+# the device-memory check.
+torch = pytest.importorskip("torch")
+
+
+def _t(n, dtype):
+    return torch.zeros(n, dtype=dtype)
+
+
+@pytest.mark.parametrize("case", ["S_bf16", "S_1d", "mask_short", "mask_i8", "offs_short",
+                                  "offs_i32", "tau_f64"])
+def test_select_binding_rejects(case):
+    S = torch.zeros(4, 10, dtype=torch.float32)
+    kw = {}
+    if case == "S_bf16":
+        S = S.to(torch.bfloat16)
+    elif case == "S_1d":
+        S = torch.zeros(40, dtype=torch.float32)
+    elif case == "mask_short":
+        kw["mask"] = _t(39, torch.uint8)
+    elif case == "mask_i8":
+        kw["mask"] = _t(40, torch.int8)
+    elif case == "offs_short":
+        kw["head_offsets"] = _t(4, torch.int64)
+    elif case == "offs_i32":
+        kw["head_offsets"] = _t(5, torch.int32)
+    elif case == "tau_f64":
+        kw["tau"] = _t(1, torch.float64)
+    full = dict(mask=_t(40, torch.uint8), head_offsets=_t(5, torch.int64), tau=_t(1, torch.float32))
+    full.update(kw)
+    name = {"S_bf16": "S", "S_1d": "S", "mask_short": "mask", "mask_i8": "mask",
+            "offs_short": "head_offsets", "offs_i32": "head_offsets", "tau_f64": "tau"}[case]
+    with pytest.raises((TypeError, ValueError), match=name) as e:
+        kvz.kvz_select_threshold(S, 5, **full)
+    assert "device tensor" not in str(e.value)
+
+
+def test_select_binding_reaches_device_check_when_valid():
+    """Control for the cases above: valid CPU arguments fail only at the
+    device-memory check."""
+    with pytest.raises(ValueError, match="device tensor"):
+        kvz.kvz_select_threshold(torch.zeros(4, 10), 5, _t(40, torch.uint8), _t(5, torch.int64),
+                                 _t(1, torch.float32), ws=_t(256, torch.uint8))
+
+
+@pytest.mark.parametrize("case", ["v_shape", "v_dtype", "mask_short", "mask_f32", "offs_short",
+                                  "offs_i32", "kout_dtype", "kout_width", "vout_rows", "idx_i64",
+                                  "idx_rows", "begin_neg", "mask_short_for_begin"])
+def test_compact_binding_rejects(case):
+    H, n_c, d, K = 2, 10, 64, 6
+    kc = torch.zeros(H, n_c, d, dtype=torch.bfloat16)
+    a = dict(k_ctx=kc, v_ctx=kc.clone(), mask=_t(H * n_c, torch.uint8),
+             head_offsets=_t(H + 1, torch.int64), k_out=torch.zeros(K, d, dtype=torch.bfloat16),
+             v_out=torch.zeros(K, d, dtype=torch.bfloat16), idx_out=_t(K, torch.int32),
+             head_begin=0)
+    if case == "v_shape":
+        a["v_ctx"] = torch.zeros(H, n_c, d + 64, dtype=torch.bfloat16)
+    elif case == "v_dtype":
+        a["v_ctx"] = kc.float()
+    elif case == "mask_short":
+        a["mask"] = _t(H * n_c - 1, torch.uint8)
+    elif case == "mask_f32":
+        a["mask"] = _t(H * n_c, torch.float32)
+    elif case == "offs_short":
+        a["head_offsets"] = _t(H, torch.int64)
+    elif case == "offs_i32":
+        a["head_offsets"] = _t(H + 1, torch.int32)
+    elif case == "kout_dtype":
+        a["k_out"] = torch.zeros(K, d, dtype=torch.float32)
+    elif case == "kout_width":
+        a["k_out"] = torch.zeros(K, d // 2, dtype=torch.bfloat16)
+    elif case == "vout_rows":
+        a["v_out"] = torch.zeros(K - 1, d, dtype=torch.bfloat16)
+    elif case == "idx_i64":
+        a["idx_out"] = _t(K, torch.int64)
+    elif case == "idx_rows":
+        a["idx_out"] = _t(K + 1, torch.int32)
+    elif case == "begin_neg":
+        a["head_begin"] = -1
+    elif case == "mask_short_for_begin":
+        a["head_begin"] = 3       # heads 3..4 need a mask of 5 * n_c entries
+    name = {"v_shape": "v_ctx", "v_dtype": "v_ctx", "mask_short": "mask", "mask_f32": "mask",
+            "offs_short": "head_offsets", "offs_i32": "head_offsets", "kout_dtype": "k_out",
+            "kout_width": "k_out", "vout_rows": "rows", "idx_i64": "idx_out", "idx_rows": "rows",
+            "begin_neg": "head_begin", "mask_short_for_begin": "mask"}[case]
+    with pytest.raises((TypeError, ValueError), match=name) as e:
+        kvz.kvz_compact(**a, ws=_t(256, torch.uint8))
+    assert "device tensor" not in str(e.value)
+
+
+def test_compact_binding_reaches_device_check_when_valid():
+    kc = torch.zeros(2, 10, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="device tensor"):
+        kvz.kvz_compact(kc, kc.clone(), _t(20, torch.uint8), _t(3, torch.int64),
+                        torch.zeros(6, 64, dtype=torch.bfloat16),
+                        torch.zeros(6, 64, dtype=torch.bfloat16), _t(6, torch.int32),
+                        ws=_t(256, torch.uint8))
+
+
+@pytest.mark.parametrize("fn", ["head", "token"])
+@pytest.mark.parametrize("case", ["S_bf16", "S_1d", "out_short", "out_f64"])
+def test_head_token_binding_rejects(fn, case):
+    S = torch.zeros(4, 10, dtype=torch.float32)
+    out = None
+    if case == "S_bf16":
+        S = S.to(torch.bfloat16)
+    elif case == "S_1d":
+        S = torch.zeros(40, dtype=torch.float32)
+    elif case == "out_short":
+        out = _t(3 if fn == "head" else 9, torch.float32)
+    elif case == "out_f64":
+        out = _t(4 if fn == "head" else 10, torch.float64)
+    f = kvz.kvz_head_scores if fn == "head" else kvz.kvz_token_scores
+    name = "out" if case.startswith("out") else "S"
+    with pytest.raises((TypeError, ValueError), match=name) as e:
+        f(S, out=out)
+    assert "device tensor" not in str(e.value)
+    if out is not None or case != "S_bf16":
+        return
+    with pytest.raises(ValueError, match="device tensor"):   # control: valid arguments
+        f(torch.zeros(4, 10))
