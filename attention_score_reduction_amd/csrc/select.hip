@@ -82,7 +82,7 @@ __global__ void sel_init(uint32_t* __restrict__ hist, uint32_t* __restrict__ joi
   }
 }
 
-// full read, histogram of the top 11 bits
+// full read, histogram of the top 12 bits (bits 31..20)
 __global__ __launch_bounds__(TPB) void sel_hist0(const float* __restrict__ S, long long N,
                                                  uint32_t* __restrict__ hist) {
   // HR copies of every bin in consecutive banks, copy = lane % HR: lanes of
@@ -125,8 +125,8 @@ __global__ __launch_bounds__(TPB) void sel_hist0(const float* __restrict__ S, lo
   }
 }
 
-// full read, scores whose top bits equal b0: LDS histogram of bits 20..10 and
-// global joint histogram of bits 20..0
+// full read, scores whose top 12 bits equal b0: LDS histogram of bits 19..10
+// and global joint histogram of bits 19..0
 __global__ __launch_bounds__(TPB) void sel_hist12(const float* __restrict__ S, long long N,
                                                   uint32_t* __restrict__ hist1,
                                                   uint32_t* __restrict__ joint,

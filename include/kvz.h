@@ -249,7 +249,11 @@ KVZ_API kvz_status kvz_decode_packed(kvz_dtype dt, int64_t n_heads, int G, int d
                                      void* ws, size_t ws_bytes, void* stream);
 
 /* ------------------------------------------------------------------------
- * Optional kernel timer (measurement only; not thread-safe).
+ * Optional kernel timer (measurement only).
+ * The timer is process-global state and is not thread-safe: enable, read and
+ * disable it from one thread, with no launching call running on another
+ * thread meanwhile.  Disabled (the default), it costs one branch per launch
+ * and every other call is reentrant.
  * While enabled, every kernel the library launches is bracketed by a pair of
  * HIP events on its stream.  kvz_prof_read() synchronises those events and
  * returns, for the kernel named `name` ("score_pass1", "score_combine",

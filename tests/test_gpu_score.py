@@ -89,7 +89,7 @@ def test_chunk_order_and_repeat_are_bitwise_invariant():
     assert np.array_equal(a, b) and np.array_equal(a, c) and np.array_equal(a, d)
 
 
-def test_group_split_is_bitwise_max_of_single_query_heads():
+def test_group_split_equals_max_of_single_query_heads():
     H, G, d, n_c, n_in = 2, 4, 128, 900, 260
     rng = np.random.default_rng(6)
     from attention_score_reduction_amd.inputs import bf16_bits
@@ -105,7 +105,8 @@ def test_group_split_is_bitwise_max_of_single_query_heads():
         kvz.kvz_score_chunk(to_dev(np.ascontiguousarray(q[:, g:g + 1]), "bf16"), kc_d, ki_d, Sg, 16)
         parts.append(Sg.cpu().numpy())
     # the row log-sum-exp of a row does not depend on G, and the column max of
-    # a union of rows is the max of the column maxima
+    # a union of rows is the max of the column maxima; the two launches split
+    # the key axis differently, so the lse may differ in its last bits
     np.testing.assert_allclose(S.cpu().numpy(), np.maximum.reduce(parts), rtol=2e-6, atol=0)
 
 
