@@ -41,6 +41,12 @@ def lib():
     global _lib
     if _lib is not None:
         return _lib
+    # torch ships its own HIP runtime under the same soname (libamdhip64.so.7);
+    # loading torch first makes libkvz bind to that runtime, so the streams
+    # and device pointers torch hands over belong to the runtime that
+    # launches the kernels.  Opened the other way round, the process would
+    # hold two HIP runtimes and every launch on a torch stream would fail.
+    import torch  # noqa: F401
     if not os.path.exists(LIB_PATH):
         raise RuntimeError(
             f"{LIB_PATH} is missing: build it with `python -c 'import __graft_entry__ as g; g.build()'`"

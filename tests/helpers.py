@@ -49,3 +49,114 @@ def oracle_layer_scores(gen, layer, heads, chunk_ids=None):
         q, kin = gen.chunk_inputs(layer, k, heads)
         ras.score_chunk(ras.to_f64(q, wl.dtype), kc64, ras.to_f64(kin, wl.dtype), scale, S)
     return S
+
+
+# ---------------------------------------------------------------------------
+# oracle on a process pool (one BLAS thread per worker)
+# ---------------------------------------------------------------------------
+
+def pool_workers():
+    """Worker count: every host core, at most 16 (a GPU machine's CPU share)."""
+    import os
+    return max(1, min(16, os.cpu_count() or 1))
+
+
+def oracle_job(args):
+    """Oracle scores of one job: (workload name, overrides, layer, heads,
+    chunk ids) -> float64 [len(heads)][n_c].  Runs in a pool worker."""
+    from threadpoolctl import threadpool_limits
+
+    from attention_score_reduction_amd.inputs import WORKLOADS, HostGen
+    name, overrides, layer, heads, chunk_ids = args
+    wl = WORKLOADS[name].with_(**overrides) if overrides else WORKLOADS[name]
+    with threadpool_limits(1):
+        return oracle_layer_scores(HostGen(wl), layer, list(heads), chunk_ids)
+
+
+def start_pool():
+    """A spawn-context pool: the workers start fresh interpreters, so nothing
+    of the parent's GPU state is inherited."""
+    import multiprocessing as mp
+    return mp.get_context("spawn").Pool(pool_workers())
+
+
+def live(config, msg):
+    """Print past pytest's output capture (progress of long waits)."""
+    capman = config.pluginmanager.getplugin("capturemanager") if config else None
+    if capman is not None:
+        with capman.global_and_fixture_disabled():
+            print(msg, flush=True)
+    else:
+        print(msg, flush=True)
+
+
+def wait_all(results, config, what, every_s=15.0):
+    """Block on a list of AsyncResults, printing progress every every_s."""
+    import time
+    t0 = last = time.time()
+    while not all(r.ready() for r in results):
+        time.sleep(0.5)
+        if time.time() - last >= every_s:
+            last = time.time()
+            done = sum(r.ready() for r in results)
+            live(config, f"[oracle] {what}: {done}/{len(results)} jobs done, {last - t0:.0f} s")
+    return [r.get() for r in results]
+
+
+def assert_relative_close(gpu, ref, floor=1e-4, rtol=1e-2, what="S"):
+    """Every score whose reference is at least `floor` is within rtol of it
+    (a proportional error in a row's log-sum-exp cannot hide under the
+    absolute tolerance)."""
+    gpu = np.asarray(gpu, np.float64)
+    ref = np.asarray(ref, np.float64)
+    sel = ref >= floor
+    rel = np.abs(gpu[sel] - ref[sel]) / ref[sel]
+    worst = rel.max() if rel.size else 0.0
+    print(f"{what}: {int(sel.sum())} scores >= {floor}, max rel err {worst:.3e}", flush=True)
+    assert worst <= rtol, f"{what}: max relative error {worst:.3e} > {rtol} on scores >= {floor}"
+    return worst
+
+
+def mask_agreement_at(gpu, ref, ratio):
+    """Fraction of keys on which (ref >= tau) and (gpu >= tau) agree, tau the
+    keep-ratio quantile of the GPU's scores (the value of the
+    round(ratio*n)-th largest)."""
+    g = np.asarray(gpu, np.float64).reshape(-1)
+    r = np.asarray(ref, np.float64).reshape(-1)
+    k = max(1, min(g.size, int(math.floor(ratio * g.size + 0.5))))
+    tau = np.sort(g)[::-1][k - 1]
+    agree = np.mean((g >= tau) == (r >= tau))
+    return float(agree), float(tau)
+
+
+def check_selection_end_to_end(s_gpu, s_ref, K, n_heads, n_c, kc_all, vc_all, dtype, mask, offs,
+                               tau, ko, vo, idx):
+    """The selection and compaction criteria on one scored cache:
+    (1) mask, head offsets, tau and the packed K/V/idx are bit-exact against
+        the oracle's selection and compaction fed the GPU's own scores;
+    (2) the mask agrees with the oracle's selection on its own fp64 scores on
+        at least 99.9% of entries, every disagreement within the score
+        tolerance of the oracle's threshold.
+    Device outputs are passed in as tensors; returns the agreement."""
+    import torch
+    rm, ro, rt = ras.select(np.asarray(s_gpu, np.float32).reshape(-1), n_heads, n_c, K)
+    m = mask.cpu().numpy()
+    assert np.array_equal(m, rm), f"mask differs at {np.nonzero(m != rm)[0][:10]}"
+    assert np.array_equal(offs.cpu().numpy(), ro), "head offsets differ"
+    t = float(tau.cpu()[0])
+    assert t == np.float32(rt) or (K == 0 and math.isinf(t)), (t, rt)
+    rko, rvo, ridx = ras.compact(kc_all, vc_all, rm, ro)
+    gk = bits_of(ko) if dtype == "bf16" else ko.cpu().numpy()
+    gv = bits_of(vo) if dtype == "bf16" else vo.cpu().numpy()
+    assert np.array_equal(gk.view(np.uint8), rko.view(np.uint8)), "packed K differs"
+    assert np.array_equal(gv.view(np.uint8), rvo.view(np.uint8)), "packed V differs"
+    assert np.array_equal(idx.cpu().numpy(), ridx), "packed positions differ"
+    em, _, et = ras.select(np.asarray(s_ref, np.float64).reshape(-1), n_heads, n_c, K)
+    dis = np.nonzero(em != rm)[0]
+    agree = 1.0 - dis.size / em.size
+    print(f"mask agreement {agree:.6f} ({dis.size} of {em.size}), tau_ref {et:.6e}", flush=True)
+    assert agree >= 0.999
+    near = np.abs(np.asarray(s_ref).reshape(-1)[dis] - et) <= ATOL + RTOL * et
+    assert near.all(), "a disagreement lies outside the score tolerance of tau"
+    del torch
+    return agree

@@ -89,6 +89,29 @@ def test_small_bf16_shapes(case):
         assert_scores_close(O[k], Or[k], atol=O_ATOL, rtol=O_RTOL, what=f"{name} O chunk {k}")
 
 
+F32_CASES = [
+    # (name, H, G, d, n_c, chunk, n_prompt, sigma, sink): random fp32 inputs
+    ("f32_d128_g2", 2, 2, 128, 700, 300, 16, 0.5, True),
+    ("f32_d256_g2", 1, 2, 256, 520, 200, 8, 1.0, False),
+]
+
+
+@pytest.mark.parametrize("case", F32_CASES, ids=[c[0] for c in F32_CASES])
+def test_small_f32_shapes(case):
+    """The fp32 path of the fused call at d = 128 and 256 on random inputs,
+    every chunk: S to 1e-6 + 1e-4 |ref|, O to 1e-5 + 1e-4 |O|."""
+    name, H, G, d, n_c, chunk, n_p, sig, sink = case
+    wl = Workload(name, 25, 1, H, G, d, n_c, chunk, n_p, 0.3, dtype="f32",
+                  key_lognormal_sigma=sig, sink=sink)
+    gen = HostGen(wl)
+    ids = list(range(len(wl.chunks())))
+    S, O = run_chunks(gen, 0, ids)
+    Sr, Or = oracle_chunks(gen, 0, ids, list(range(H)))
+    assert_scores_close(S, Sr, atol=1e-6, rtol=1e-4, what=f"{name} S")
+    for k in ids:
+        assert_scores_close(O[k], Or[k], atol=1e-5, rtol=1e-4, what=f"{name} O chunk {k}")
+
+
 def test_scores_equal_kvz_score_chunk_bitwise():
     """The fused call's score update is the plain score call's, bit for bit."""
     wl = Workload("same", 22, 1, 2, 4, 128, 1100, 400, 16, 0.3, key_lognormal_sigma=0.5, sink=True)

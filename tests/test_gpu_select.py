@@ -7,9 +7,9 @@ import numpy as np
 import pytest
 
 from attention_score_reduction_amd import kvz
-from attention_score_reduction_amd.inputs import WORKLOADS, HostGen, Workload, bf16_bits
+from attention_score_reduction_amd.inputs import WORKLOADS, HostGen, Workload
 from oracle import ras
-from tests.helpers import ATOL, RTOL, bits_of, oracle_layer_scores, to_dev
+from tests.helpers import bits_of, check_selection_end_to_end, oracle_layer_scores, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -179,25 +179,9 @@ def _end_to_end(wl, layers, heads_checked=None):
     kvz.kvz_compact(to_dev(kc_all, wl.dtype), to_dev(vc_all, wl.dtype), mask, offs, ko, vo, idx)
     torch.cuda.synchronize()
     s_gpu = S.cpu().numpy()
-    # (1) bit-exact given the GPU's scores
-    rm, ro, rt = ras.select(s_gpu.reshape(-1), n_heads, n_c, K)
-    assert np.array_equal(mask.cpu().numpy(), rm)
-    assert np.array_equal(offs.cpu().numpy(), ro)
-    rko, rvo, ridx = ras.compact(kc_all, vc_all, rm, ro)
-    gk = bits_of(ko) if wl.dtype == "bf16" else ko.cpu().numpy()
-    gv = bits_of(vo) if wl.dtype == "bf16" else vo.cpu().numpy()
-    assert np.array_equal(gk.view(np.uint8), rko.view(np.uint8))
-    assert np.array_equal(gv.view(np.uint8), rvo.view(np.uint8))
-    assert np.array_equal(idx.cpu().numpy(), ridx)
-    # (2) agreement with the oracle end to end
     s_ref = np.concatenate(refs)
-    em, _, et = ras.select(s_ref.reshape(-1), n_heads, n_c, K)
-    dis = np.nonzero(em != rm)[0]
-    agree = 1.0 - dis.size / em.size
-    print(f"{wl.name}: mask agreement {agree:.6f} ({dis.size} of {em.size}), tau_ref {et:.4e}")
-    assert agree >= 0.999
-    near = np.abs(s_ref.reshape(-1)[dis] - et) <= ATOL + RTOL * et
-    assert near.all()
+    check_selection_end_to_end(s_gpu, s_ref, K, n_heads, n_c, kc_all, vc_all, wl.dtype, mask,
+                               offs, tau, ko, vo, idx)
 
 
 def test_end_to_end_tiny_fp32():
