@@ -21,7 +21,7 @@ AGG = {"max": KVZ_AGG_MAX, "sum": KVZ_AGG_SUM, "raw": KVZ_AGG_RAW_MAX}
 # every symbol declared in include/kvz.h
 SYMBOLS = (
     "kvz_build_id", "kvz_status_string", "kvz_score_chunk_workspace", "kvz_score_chunk", "kvz_score_chunk_ex",
-    "kvz_score_chunk_attn_workspace", "kvz_score_chunk_attn",
+    "kvz_score_chunk_attn_workspace", "kvz_score_chunk_attn", "kvz_score_chunk_noalloc",
     "kvz_keep_count", "kvz_select_workspace", "kvz_select_threshold", "kvz_compact_workspace",
     "kvz_compact", "kvz_head_scores", "kvz_token_scores", "kvz_decode_workspace",
     "kvz_decode_packed", "kvz_prof_enable", "kvz_prof_read",
@@ -73,6 +73,9 @@ def lib():
     L.kvz_score_chunk_ex.argtypes = [c_int, c_int, c_int, c_int, c_int, c_int, c_int, c_int, c_p,
                                      c_p, c_p, c_f, c_p, c_p, c_sz, c_p]
     L.kvz_score_chunk_ex.restype = c_int
+    L.kvz_score_chunk_noalloc.argtypes = [c_int, c_int, c_int, c_int, c_int, c_int, c_int, c_p, c_p,
+                                          c_p, c_f, c_p, c_p]
+    L.kvz_score_chunk_noalloc.restype = c_int
     L.kvz_score_chunk_attn_workspace.argtypes = [c_int, c_int, c_int, c_int, c_int, c_int]
     L.kvz_score_chunk_attn_workspace.restype = c_sz
     L.kvz_score_chunk_attn.argtypes = [c_int, c_int, c_int, c_int, c_int, c_int, c_int, c_p, c_p,
@@ -210,6 +213,32 @@ def kvz_score_chunk_ex(q, k_ctx, k_in, S, n_prompt, agg="max", scale=None, ws=No
                                   _ptr(S, "S"), _ptr(ws, "ws"), ws.numel() * ws.element_size(),
                                   _stream(stream))
     _check(st, "kvz_score_chunk_ex")
+    return S
+
+
+NOALLOC_SCRATCH_BYTES = 16 << 20   # KVZ_NOALLOC_SCRATCH_BYTES
+
+
+def kvz_score_chunk_noalloc(q, k_ctx, k_in, S, n_prompt, scale=None, stream=None):
+    """kvz_score_chunk without a workspace: the library's fixed device scratch
+    array holds it, and nothing is allocated (for code under graph capture
+    or loops that must not allocate).  Calls overlapping on one device race."""
+    import torch
+    H, G, n_in, d = q.shape
+    n_c = k_ctx.shape[1]
+    if tuple(k_ctx.shape) != (H, n_c, d) or tuple(k_in.shape) != (H, n_in, d):
+        raise ValueError("shape mismatch between q, k_ctx and k_in")
+    if tuple(S.shape) != (H, n_c) or S.dtype != torch.float32:
+        raise ValueError("S must be fp32 [H][n_c]")
+    if k_ctx.dtype != q.dtype or k_in.dtype != q.dtype:
+        raise TypeError("q, k_ctx and k_in must share a dtype")
+    dt = _dtype_code(q)
+    if scale is None:
+        scale = d ** -0.5
+    st = lib().kvz_score_chunk_noalloc(dt, H, G, d, n_c, int(n_prompt), n_in, _ptr(q, "q"),
+                                       _ptr(k_ctx, "k_ctx"), _ptr(k_in, "k_in"), float(scale),
+                                       _ptr(S, "S"), _stream(stream))
+    _check(st, "kvz_score_chunk_noalloc")
     return S
 
 

@@ -129,6 +129,27 @@ KVZ_API kvz_status kvz_score_chunk_ex(kvz_dtype dt, kvz_aggregate agg, int H, in
                                       void* ws, size_t ws_bytes, void* stream);
 
 /* ------------------------------------------------------------------------
+ * kvz_score_chunk for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ *
+ * Same arguments, S update, limits and errors as kvz_score_chunk, without
+ * the workspace: the library keeps a fixed scratch array of
+ * KVZ_NOALLOC_SCRATCH_BYTES in device memory (one per device it runs on,
+ * held until the process ends) and this call allocates nothing.  A problem
+ * whose workspace (kvz_score_chunk_workspace) exceeds that size is rejected
+ * with KVZ_ERR_WORKSPACE before anything is launched; every workload up to
+ * 8 KV heads, G = 5 and 2K-token chunks of a 170K context fits.  Calls that
+ * overlap on one device share the scratch array and race: serialise them
+ * (one stream, or events).  Nothing carries over between calls.
+ * ---------------------------------------------------------------------- */
+#define KVZ_NOALLOC_SCRATCH_BYTES (16u << 20)
+
+KVZ_API kvz_status kvz_score_chunk_noalloc(kvz_dtype dt, int H, int G, int d, int n_c,
+                                           int n_prompt, int n_in, const void* q,
+                                           const void* k_ctx, const void* k_in, float scale,
+                                           float* S, void* stream);
+
+/* ------------------------------------------------------------------------
  * Scoring of one chunk together with the chunk's attention output: the
  * fused reconstruction attention (rebuttal, computational analysis: the
  * scoring stage is a full forward over [repeat prompt; chunk], one MLP pass

@@ -321,3 +321,40 @@ def test_head_token_binding_rejects(fn, case):
         return
     with pytest.raises(ValueError, match="device tensor"):   # control: valid arguments
         f(torch.zeros(4, 10))
+
+
+def _noalloc(**kw):
+    a = dict(dt=0, H=2, G=4, d=128, n_c=100, n_prompt=4, n_in=20, q=FAKE, kc=FAKE, ki=FAKE,
+             scale=0.1, S=FAKE, stream=None)
+    a.update(kw)
+    return kvz.lib().kvz_score_chunk_noalloc(a["dt"], a["H"], a["G"], a["d"], a["n_c"],
+                                             a["n_prompt"], a["n_in"], a["q"], a["kc"], a["ki"],
+                                             a["scale"], a["S"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(d=96), kvz.KVZ_ERR_UNSUPPORTED), (dict(dt=7), kvz.KVZ_ERR_UNSUPPORTED),
+    (dict(H=0), kvz.KVZ_ERR_INVALID_ARG), (dict(n_prompt=21), kvz.KVZ_ERR_INVALID_ARG),
+    (dict(q=None), kvz.KVZ_ERR_INVALID_ARG), (dict(S=MIS), kvz.KVZ_ERR_INVALID_ARG),
+    (dict(scale=0.0), kvz.KVZ_ERR_INVALID_ARG), (dict(d=256, n_c=4194304), kvz.KVZ_ERR_INVALID_ARG),
+    # 4 KV heads x 64 query heads x 8192 rows need ~38 MB of scratch: more
+    # than the fixed array holds, rejected before any launch
+    (dict(H=4, G=64, n_in=8192, n_prompt=16, n_c=1000), kvz.KVZ_ERR_WORKSPACE),
+])
+def test_noalloc_validation(kw, status):
+    assert _noalloc(**kw) == status
+
+
+def test_noalloc_scratch_covers_the_workloads():
+    """The fixed scratch array holds the workspace of every workload's chunk
+    (8 KV heads; G = 4 / 5 / 2; 2K / 2K / 1K-token chunks of 128K / 120K /
+    170K contexts), and the rejection above is for a larger problem."""
+    cap = kvz.NOALLOC_SCRATCH_BYTES
+    for (G, n_in, d, n_c) in ((4, 2064, 128, 131072), (5, 2064, 128, 120000),
+                              (2, 1040, 256, 170000), (4, 2064, 128, 8192), (2, 136, 64, 512)):
+        need = kvz.kvz_score_chunk_workspace(kvz.KVZ_BF16, 8, G, n_in, d, n_c)
+        assert 0 < need <= cap, (G, n_in, d, n_c, need)
+    assert kvz.kvz_score_chunk_workspace(kvz.KVZ_BF16, 32, 4, 2064, 128, 131072) <= cap
+    assert kvz.kvz_score_chunk_workspace(kvz.KVZ_BF16, 4, 64, 8192, 128, 1000) > cap
+    hdr = open(os.path.join(ROOT, "include", "kvz.h")).read()
+    assert re.search(r"#define KVZ_NOALLOC_SCRATCH_BYTES \(16u << 20\)", hdr)

@@ -1,0 +1,43 @@
+"""kvz_score_chunk_noalloc (fixed device scratch, no allocation) against
+kvz_score_chunk (caller workspace) through the C ABI: two calls in a row, the
+second with a smaller problem, each bit-identical to the workspace call (the
+same kernels and launch plan run on the same inputs)."""
+import math
+
+import numpy as np
+import pytest
+
+from attention_score_reduction_amd import kvz
+from attention_score_reduction_amd.inputs import HostGen, Workload
+from tests.helpers import to_dev
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+def _case(wl, chunk_ids):
+    gen = HostGen(wl)
+    kc, _ = gen.context(0)
+    kc_d = to_dev(kc, wl.dtype)
+    S_ws = torch.zeros(wl.heads, wl.n_ctx, dtype=torch.float32, device="cuda")
+    S_na = torch.full((wl.heads, wl.n_ctx), 0.0, dtype=torch.float32, device="cuda")
+    scale = 1 / math.sqrt(wl.head_dim)
+    for k in chunk_ids:
+        q, kin = gen.chunk_inputs(0, k)
+        qd, kd = to_dev(q, wl.dtype), to_dev(kin, wl.dtype)
+        kvz.kvz_score_chunk(qd, kc_d, kd, S_ws, wl.n_prompt, scale)
+        kvz.kvz_score_chunk_noalloc(qd, kc_d, kd, S_na, wl.n_prompt, scale)
+    torch.cuda.synchronize()
+    return S_ws.cpu().numpy(), S_na.cpu().numpy()
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_noalloc_matches_workspace_call_twice_shrinking(dtype):
+    big = Workload("na_big", 51, 1, 4, 4, 128, 6000, 1500, 16, 0.3, dtype=dtype,
+                   key_lognormal_sigma=0.5, sink=True)
+    small = Workload("na_small", 52, 1, 2, 2, 64, 900, 300, 8, 0.3, dtype=dtype, sink=True)
+    for wl, ids in ((big, [0, 3]), (small, [0, 2])):
+        a, b = _case(wl, ids)
+        assert np.array_equal(a, b), f"{wl.name}: noalloc scores differ from the workspace call"
+        assert np.all(a > 0) and np.all(a <= 1)
