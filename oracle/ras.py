@@ -217,6 +217,49 @@ def select(S_flat, n_heads: int, n_c: int, K: int):
 
 
 # ---------------------------------------------------------------------------
+# structured eviction variants built on the same scores
+# ---------------------------------------------------------------------------
+
+def head_evict(S2d, K_heads: int, n_sink: int, n_recent: int):
+    """Context-independent head-level eviction ([rebuttal] answer on how the
+    head-level scores were computed: a head's score is the max of S along the
+    sequence axis; [blog] 5.4: KVzip's scores drive head-level eviction in
+    place of DuoAttention's optimised head scores).
+
+    The K_heads heads with the highest head scores keep every token; ties go
+    to the lower flat head index (the order of select()).  The pages do not
+    say what an evicted head keeps; here, as for DuoAttention's streaming
+    heads, it keeps its first n_sink and its last n_recent tokens.
+    Returns (mask uint8 [N], head_offsets int64 [n_heads + 1],
+    head_keep uint8 [n_heads])."""
+    S2d = np.asarray(S2d)
+    n_heads, n_c = S2d.shape
+    head_keep, _, _ = select(head_scores(S2d), 1, n_heads, K_heads)
+    j = np.arange(n_c)
+    window = (j < n_sink) | (j >= n_c - n_recent)
+    mask = np.where(head_keep[:, None] == 1, True, window[None, :]).astype(np.uint8)
+    budget = mask.sum(axis=1, dtype=np.int64)
+    offsets = np.zeros(n_heads + 1, np.int64)
+    offsets[1:] = np.cumsum(budget)
+    return mask.reshape(-1), offsets, head_keep
+
+
+def token_evict(S2d, K_tokens: int):
+    """Token-level eviction ([blog] 4.3.3: one score per token, the max over
+    every layer and head; sorting those scores decides which tokens stay).
+
+    The K_tokens positions with the highest token scores (ties: lower
+    position first) are kept in every head.  Returns (mask uint8 [N],
+    head_offsets int64 [n_heads + 1], token_keep uint8 [n_c])."""
+    S2d = np.asarray(S2d)
+    n_heads, n_c = S2d.shape
+    token_keep, _, _ = select(token_scores(S2d), 1, n_c, K_tokens)
+    mask = np.tile(token_keep, n_heads)
+    offsets = np.arange(n_heads + 1, dtype=np.int64) * int(token_keep.sum())
+    return mask, offsets, token_keep
+
+
+# ---------------------------------------------------------------------------
 # decode attention over a packed per-head cache  ([abstract] and [atlas] Key
 # results: the compressed cache cuts FlashAttention decode latency about 2x;
 # [rebuttal] computational analysis: decode attention latency against the

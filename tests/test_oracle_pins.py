@@ -472,3 +472,79 @@ def test_attention_output_one_hot_values_give_probabilities():
     for g in range(G):
         P = ras.chunk_probabilities(q[0, g], kc[0], ki[0], 0.5)
         np.testing.assert_allclose(O[0, g], P, rtol=0, atol=1e-15)
+
+
+# ---------------------------------------------------------------------------
+# head-level and token-level eviction
+# ---------------------------------------------------------------------------
+
+def _brute_head_evict(S, K_heads, n_sink, n_recent):
+    """Pure-Python reference: rank heads by (max score desc, index asc)."""
+    n_heads, n_c = len(S), len(S[0])
+    score = [max(row) for row in S]
+    order = sorted(range(n_heads), key=lambda h: (-score[h], h))
+    kept = set(order[:K_heads])
+    mask = []
+    for h in range(n_heads):
+        for j in range(n_c):
+            mask.append(1 if (h in kept or j < n_sink or j >= n_c - n_recent) else 0)
+    offs = [0]
+    for h in range(n_heads):
+        offs.append(offs[-1] + sum(mask[h * n_c:(h + 1) * n_c]))
+    return mask, offs, [1 if h in kept else 0 for h in range(n_heads)]
+
+
+@pytest.mark.parametrize("K_heads,n_sink,n_recent", [(3, 2, 4), (0, 1, 1), (7, 0, 0), (2, 0, 5),
+                                                      (4, 6, 9), (1, 20, 0), (5, 11, 11)])
+def test_head_evict_brute_force(K_heads, n_sink, n_recent):
+    rng = np.random.default_rng(80 + K_heads)
+    S = (rng.integers(0, 5, (7, 13)) / 8.0)          # equal head maxima happen: ties
+    m, o, keep = ras.head_evict(S, K_heads, n_sink, n_recent)
+    bm, bo, bk = _brute_head_evict(S.tolist(), K_heads, n_sink, n_recent)
+    assert m.tolist() == bm and o.tolist() == bo and keep.tolist() == bk
+    # closed form of the kept count: whole heads plus two windows per evicted head
+    n_c = S.shape[1]
+    w = min(n_c, min(n_sink, n_c) + min(n_recent, n_c))
+    assert int(o[-1]) == K_heads * n_c + (S.shape[0] - K_heads) * w
+
+
+def test_head_evict_ties_go_to_lower_index():
+    S = np.zeros((4, 5))
+    S[1, 2] = S[3, 0] = S[2, 4] = 0.5                 # heads 1, 2, 3 tie at 0.5
+    _, _, keep = ras.head_evict(S, 2, 0, 0)
+    assert keep.tolist() == [0, 1, 1, 0]
+
+
+def _brute_token_evict(S, K_tokens):
+    n_heads, n_c = len(S), len(S[0])
+    score = [max(S[h][j] for h in range(n_heads)) for j in range(n_c)]
+    kept = set(sorted(range(n_c), key=lambda j: (-score[j], j))[:K_tokens])
+    mask = [1 if j in kept else 0 for h in range(n_heads) for j in range(n_c)]
+    return mask, [h * K_tokens for h in range(n_heads + 1)], [1 if j in kept else 0
+                                                              for j in range(n_c)]
+
+
+@pytest.mark.parametrize("K_tokens", [0, 1, 6, 17, 19])
+def test_token_evict_brute_force(K_tokens):
+    rng = np.random.default_rng(90 + K_tokens)
+    S = rng.integers(0, 6, (5, 19)) / 16.0
+    m, o, keep = ras.token_evict(S, K_tokens)
+    bm, bo, bk = _brute_token_evict(S.tolist(), K_tokens)
+    assert m.tolist() == bm and o.tolist() == bo and keep.tolist() == bk
+    # every head keeps the same positions, K_tokens of them
+    assert np.all(m.reshape(5, 19) == keep[None, :]) and int(keep.sum()) == K_tokens
+
+
+def test_evictions_compose_with_compaction():
+    """The packed cache of either eviction holds, per head, exactly the rows
+    its mask keeps, in ascending position."""
+    rng = np.random.default_rng(95)
+    S = rng.random((6, 40))
+    kc = rng.integers(0, 1 << 16, (6, 40, 8), dtype=np.uint16)
+    vc = rng.integers(0, 1 << 16, (6, 40, 8), dtype=np.uint16)
+    for m, o, _ in (ras.head_evict(S, 2, 3, 5), ras.token_evict(S, 9)):
+        ko, vo, idx = ras.compact(kc, vc, m, o)
+        for h in range(6):
+            js = [j for j in range(40) if m[h * 40 + j]]
+            assert idx[o[h]:o[h + 1]].tolist() == js
+            assert np.array_equal(ko[o[h]:o[h + 1]], kc[h, js])
