@@ -179,6 +179,51 @@ kvz_status kvz_token_scores(const float* S, int64_t n_heads, int n_c, float* tok
   return e == hipSuccess ? KVZ_OK : KVZ_ERR_HIP;
 }
 
+size_t kvz_select_heads_workspace(int64_t n_heads, int n_c) {
+  if (n_heads < 1 || n_c < 1 || n_heads * (int64_t)n_c >= (int64_t(1) << 31)) return 0;
+  return agg_select_workspace(n_heads);
+}
+
+kvz_status kvz_select_heads(const float* S, int64_t n_heads, int n_c, int64_t K_heads,
+                            int n_sink, int n_recent, uint8_t* mask, int64_t* head_offsets,
+                            uint8_t* head_keep, void* ws, size_t ws_bytes, void* stream) {
+  if (n_heads < 1 || n_c < 1 || n_heads * (int64_t)n_c >= (int64_t(1) << 31))
+    return KVZ_ERR_INVALID_ARG;
+  if (K_heads < 0 || K_heads > n_heads || n_sink < 0 || n_recent < 0) return KVZ_ERR_INVALID_ARG;
+  if (!S || !mask || !head_offsets || !head_keep || !ws) return KVZ_ERR_INVALID_ARG;
+  if (!aligned16(S) || !aligned16(mask) || (reinterpret_cast<uintptr_t>(head_offsets) & 7u) != 0 ||
+      (reinterpret_cast<uintptr_t>(ws) & 255u) != 0)
+    return KVZ_ERR_INVALID_ARG;
+  if (ws_bytes < agg_select_workspace(n_heads)) return KVZ_ERR_WORKSPACE;
+  clear_error();
+  const hipError_t e = select_heads_launch(S, n_heads, n_c, K_heads, n_sink, n_recent, mask,
+                                           head_offsets, head_keep, ws,
+                                           reinterpret_cast<hipStream_t>(stream));
+  return e == hipSuccess ? KVZ_OK : KVZ_ERR_HIP;
+}
+
+size_t kvz_select_tokens_workspace(int64_t n_heads, int n_c) {
+  if (n_heads < 1 || n_c < 1 || n_heads * (int64_t)n_c >= (int64_t(1) << 31)) return 0;
+  return agg_select_workspace(n_c);
+}
+
+kvz_status kvz_select_tokens(const float* S, int64_t n_heads, int n_c, int64_t K_tokens,
+                             uint8_t* mask, int64_t* head_offsets, uint8_t* token_keep, void* ws,
+                             size_t ws_bytes, void* stream) {
+  if (n_heads < 1 || n_c < 1 || n_heads * (int64_t)n_c >= (int64_t(1) << 31))
+    return KVZ_ERR_INVALID_ARG;
+  if (K_tokens < 0 || K_tokens > n_c) return KVZ_ERR_INVALID_ARG;
+  if (!S || !mask || !head_offsets || !token_keep || !ws) return KVZ_ERR_INVALID_ARG;
+  if (!aligned16(S) || !aligned16(mask) || (reinterpret_cast<uintptr_t>(head_offsets) & 7u) != 0 ||
+      (reinterpret_cast<uintptr_t>(ws) & 255u) != 0)
+    return KVZ_ERR_INVALID_ARG;
+  if (ws_bytes < agg_select_workspace(n_c)) return KVZ_ERR_WORKSPACE;
+  clear_error();
+  const hipError_t e = select_tokens_launch(S, n_heads, n_c, K_tokens, mask, head_offsets,
+                                            token_keep, ws, reinterpret_cast<hipStream_t>(stream));
+  return e == hipSuccess ? KVZ_OK : KVZ_ERR_HIP;
+}
+
 int64_t kvz_keep_count(int64_t N, double r) {
   if (N <= 0 || !(r > 0.0)) return 0;
   if (r >= 1.0) return N;
@@ -301,7 +346,7 @@ kvz_status kvz_prof_read(const char* name, int64_t* launches, double* total_ms) 
                                  "select_mask",     "compact_count",  "compact_scan",
                                  "compact_scatter", "head_scores",    "token_scores",
                                  "decode_split",    "decode_combine", "attn_pass3",
-                                 "attn_reduce"};
+                                 "attn_reduce",     "evict_mask",     "evict_offsets"};
   for (const char* k : kNames) known |= strcmp(k, name) == 0;
   if (!known) return KVZ_ERR_INVALID_ARG;
   for (const ProfRec& r : p.recs) {

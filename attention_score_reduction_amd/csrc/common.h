@@ -105,6 +105,15 @@ hipError_t head_scores_launch(const float* S, int64_t n_heads, int n_c, float* o
 hipError_t token_scores_launch(const float* S, int64_t n_heads, int n_c, float* out,
                                hipStream_t st);
 
+// structured selections on the head-level / token-level aggregates of S
+size_t agg_select_workspace(int64_t n_agg);
+hipError_t select_heads_launch(const float* S, int64_t n_heads, int n_c, int64_t K_heads,
+                               int n_sink, int n_recent, uint8_t* mask, int64_t* head_offsets,
+                               uint8_t* head_keep, void* ws, hipStream_t st);
+hipError_t select_tokens_launch(const float* S, int64_t n_heads, int n_c, int64_t K_tokens,
+                                uint8_t* mask, int64_t* head_offsets, uint8_t* token_keep,
+                                void* ws, hipStream_t st);
+
 struct SelectPlan {
   int64_t N, n_heads;
   int n_c, tiles_per_head;

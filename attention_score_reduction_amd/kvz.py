@@ -22,7 +22,9 @@ AGG = {"max": KVZ_AGG_MAX, "sum": KVZ_AGG_SUM, "raw": KVZ_AGG_RAW_MAX}
 SYMBOLS = (
     "kvz_build_id", "kvz_status_string", "kvz_score_chunk_workspace", "kvz_score_chunk", "kvz_score_chunk_ex",
     "kvz_score_chunk_attn_workspace", "kvz_score_chunk_attn", "kvz_score_chunk_noalloc",
-    "kvz_keep_count", "kvz_select_workspace", "kvz_select_threshold", "kvz_compact_workspace",
+    "kvz_keep_count", "kvz_select_workspace", "kvz_select_threshold",
+    "kvz_select_heads_workspace", "kvz_select_heads", "kvz_select_tokens_workspace",
+    "kvz_select_tokens", "kvz_compact_workspace",
     "kvz_compact", "kvz_head_scores", "kvz_token_scores", "kvz_decode_workspace",
     "kvz_decode_packed", "kvz_prof_enable", "kvz_prof_read",
 )
@@ -96,6 +98,15 @@ def lib():
     L.kvz_select_workspace.restype = c_sz
     L.kvz_select_threshold.argtypes = [c_p, c_i64, c_int, c_i64, c_p, c_p, c_p, c_p, c_sz, c_p]
     L.kvz_select_threshold.restype = c_int
+    L.kvz_select_heads_workspace.argtypes = [c_i64, c_int]
+    L.kvz_select_heads_workspace.restype = c_sz
+    L.kvz_select_heads.argtypes = [c_p, c_i64, c_int, c_i64, c_int, c_int, c_p, c_p, c_p, c_p,
+                                   c_sz, c_p]
+    L.kvz_select_heads.restype = c_int
+    L.kvz_select_tokens_workspace.argtypes = [c_i64, c_int]
+    L.kvz_select_tokens_workspace.restype = c_sz
+    L.kvz_select_tokens.argtypes = [c_p, c_i64, c_int, c_i64, c_p, c_p, c_p, c_p, c_sz, c_p]
+    L.kvz_select_tokens.restype = c_int
     L.kvz_compact_workspace.argtypes = [c_i64, c_int]
     L.kvz_compact_workspace.restype = c_sz
     L.kvz_compact.argtypes = [c_int, c_int, c_int, c_i64, c_i64, c_p, c_p, c_p, c_p, c_p, c_p, c_p,
@@ -337,6 +348,77 @@ def kvz_select_threshold(S, K, mask=None, head_offsets=None, tau=None, ws=None, 
                                     _stream(stream))
     _check(st, "kvz_select_threshold")
     return mask, head_offsets, tau
+
+
+def kvz_select_heads_workspace(n_heads, n_c) -> int:
+    return int(lib().kvz_select_heads_workspace(int(n_heads), int(n_c)))
+
+
+def kvz_select_tokens_workspace(n_heads, n_c) -> int:
+    return int(lib().kvz_select_tokens_workspace(int(n_heads), int(n_c)))
+
+
+def _agg_outputs(S, n_keep, mask, head_offsets, keep):
+    import torch
+    n_heads, n_c = S.shape
+    dev = S.device
+    if mask is None:
+        mask = torch.empty(n_heads * n_c, dtype=torch.uint8, device=dev)
+    if head_offsets is None:
+        head_offsets = torch.empty(n_heads + 1, dtype=torch.int64, device=dev)
+    if keep is None:
+        keep = torch.empty(n_keep, dtype=torch.uint8, device=dev)
+    _need(mask, "mask", torch.uint8, numel=n_heads * n_c, device=dev)
+    _need(head_offsets, "head_offsets", torch.int64, numel=n_heads + 1, device=dev)
+    return mask, head_offsets, keep
+
+
+def kvz_select_heads(S, K_heads, n_sink, n_recent, mask=None, head_offsets=None, head_keep=None,
+                     ws=None, stream=None):
+    """Head-level eviction over S [n_heads][n_c] (fp32): the K_heads heads
+    with the highest max score keep every token, the others their first
+    n_sink and last n_recent tokens.  Returns (mask uint8 [N], head_offsets
+    int64 [n_heads + 1], head_keep uint8 [n_heads]), all on the device."""
+    import torch
+    _need(S, "S", torch.float32)
+    if S.dim() != 2:
+        raise ValueError("S must be [n_heads][n_c]")
+    n_heads, n_c = S.shape
+    mask, head_offsets, head_keep = _agg_outputs(S, n_heads, mask, head_offsets, head_keep)
+    _need(head_keep, "head_keep", torch.uint8, numel=n_heads, device=S.device)
+    if ws is None:
+        ws = _ws(kvz_select_heads_workspace(n_heads, n_c), S.device)
+    _need(ws, "ws", torch.uint8, device=S.device)
+    st = lib().kvz_select_heads(_ptr(S, "S"), n_heads, n_c, int(K_heads), int(n_sink),
+                                int(n_recent), _ptr(mask, "mask"),
+                                _ptr(head_offsets, "head_offsets"), _ptr(head_keep, "head_keep"),
+                                _ptr(ws, "ws"), ws.numel() * ws.element_size(), _stream(stream))
+    _check(st, "kvz_select_heads")
+    return mask, head_offsets, head_keep
+
+
+def kvz_select_tokens(S, K_tokens, mask=None, head_offsets=None, token_keep=None, ws=None,
+                      stream=None):
+    """Token-level eviction over S [n_heads][n_c] (fp32): the K_tokens
+    positions with the highest max score over all heads are kept in every
+    head.  Returns (mask uint8 [N], head_offsets int64 [n_heads + 1],
+    token_keep uint8 [n_c]), all on the device."""
+    import torch
+    _need(S, "S", torch.float32)
+    if S.dim() != 2:
+        raise ValueError("S must be [n_heads][n_c]")
+    n_heads, n_c = S.shape
+    mask, head_offsets, token_keep = _agg_outputs(S, n_c, mask, head_offsets, token_keep)
+    _need(token_keep, "token_keep", torch.uint8, numel=n_c, device=S.device)
+    if ws is None:
+        ws = _ws(kvz_select_tokens_workspace(n_heads, n_c), S.device)
+    _need(ws, "ws", torch.uint8, device=S.device)
+    st = lib().kvz_select_tokens(_ptr(S, "S"), n_heads, n_c, int(K_tokens), _ptr(mask, "mask"),
+                                 _ptr(head_offsets, "head_offsets"),
+                                 _ptr(token_keep, "token_keep"), _ptr(ws, "ws"),
+                                 ws.numel() * ws.element_size(), _stream(stream))
+    _check(st, "kvz_select_tokens")
+    return mask, head_offsets, token_keep
 
 
 def kvz_compact(k_ctx, v_ctx, mask, head_offsets, k_out, v_out, idx_out, head_begin=0,

@@ -10,8 +10,8 @@ roofline of the dominant kernel (from HIP events recorded around each launch
 inside the timed steps), the CPU oracle's rate on a bounded sample of the
 same inputs, and the check of the timed step's outputs against the oracle.
 After the timed steps (outside the headline figure) it also measures: decode
-attention over the packed cache at several keep ratios, the fused
-attention-output call, one layer of the 120K Qwen and 170K Gemma shapes, and
+attention over the packed cache at several keep ratios, head-level and
+token-level eviction with their compaction, the fused attention-output call, one layer of the 120K Qwen and 170K Gemma shapes, and
 head-level scores of an 88K-token context.  Exits non-zero when the timed
 step's outputs disagree with the oracle.
 """
@@ -290,6 +290,65 @@ def decode_sweep(kvz, wl, S, kc_flat, vc_flat, ratios=(1.0, 0.8, 0.6, 0.4, 0.2))
                     "scores",
             "pages_context": "rebuttal decoding table (Qwen3-32B, 124K, FP8, H100): 0.45 / 0.39 / "
                              "0.34 / 0.28 / 0.23 ms at keep ratio 1 / 0.8 / 0.6 / 0.4 / 0.2"}
+
+
+def structured_evictions(kvz, wl, S, kc_flat, vc_flat, n_sink=64, n_recent=1024):
+    """Head-level eviction (the top 30% of heads by head score kept whole,
+    the others their first n_sink and last n_recent tokens) and token-level
+    eviction (the top 30% of positions by token score kept in every head) of
+    the timed step's scores, each followed by the compaction of its keep set:
+    per-kernel times, kept rows and bytes moved."""
+    import torch
+    dev = S.device
+    n_heads, n_c, d = wl.n_heads, wl.n_ctx, wl.head_dim
+    N = n_heads * n_c
+    mask = torch.empty(N, dtype=torch.uint8, device=dev)
+    offs = torch.empty(n_heads + 1, dtype=torch.int64, device=dev)
+    hk = torch.empty(n_heads, dtype=torch.uint8, device=dev)
+    tk = torch.empty(n_c, dtype=torch.uint8, device=dev)
+    ws_h = torch.empty(kvz.kvz_select_heads_workspace(n_heads, n_c), dtype=torch.uint8, device=dev)
+    ws_t = torch.empty(kvz.kvz_select_tokens_workspace(n_heads, n_c), dtype=torch.uint8,
+                       device=dev)
+    K_h = kvz.kvz_keep_count(n_heads, wl.keep_ratio)
+    K_t = kvz.kvz_keep_count(n_c, wl.keep_ratio)
+    rows_h = K_h * n_c + (n_heads - K_h) * min(n_c, n_sink + n_recent)
+    rows_t = K_t * n_heads
+    cap = max(rows_h, rows_t)
+    ko = torch.empty(cap, d, dtype=kc_flat.dtype, device=dev)
+    vo = torch.empty(cap, d, dtype=kc_flat.dtype, device=dev)
+    idx = torch.empty(cap, dtype=torch.int32, device=dev)
+    names = ("head_scores", "token_scores", "select_init", "select_hist", "select_pick",
+             "select_fixup", "select_scan", "select_mask", "select_empty", "evict_mask",
+             "evict_offsets", "compact_count", "compact_scan", "compact_scatter")
+    out = {}
+    for mode in ("heads", "tokens"):
+        rows = rows_h if mode == "heads" else rows_t
+
+        def run():
+            if mode == "heads":
+                kvz.kvz_select_heads(S, K_h, n_sink, n_recent, mask, offs, hk, ws=ws_h)
+            else:
+                kvz.kvz_select_tokens(S, K_t, mask, offs, tk, ws=ws_t)
+            kvz.kvz_compact(kc_flat, vc_flat, mask, offs, ko[:rows], vo[:rows], idx[:rows])
+
+        run()
+        torch.cuda.synchronize()
+        assert int(offs[-1].item()) == rows
+        pr = prof_window(kvz, names, run, 64)
+        # total time of each kernel name in one call (several launches for
+        # the selection's picks and scans)
+        per = {nm: round(ms * 1e3, 2) for nm, (n, ms) in pr.items()}
+        sel_us = sum(v for k, v in per.items() if not k.startswith("compact"))
+        out[mode] = {"kept_rows": rows, "kept_fraction": round(rows / N, 4),
+                     "select_us": round(sel_us, 2),
+                     "compact_us": round(sum(v for k, v in per.items() if k.startswith("compact")),
+                                         2),
+                     "per_kernel_total_us": per}
+    out["heads"]["what"] = (f"{K_h} of {n_heads} heads kept whole by head score, the others "
+                            f"keep their first {n_sink} and last {n_recent} tokens (window sizes "
+                            "are this benchmark's choice)")
+    out["tokens"]["what"] = f"{K_t} of {n_c} positions kept in every head by token score"
+    return out
 
 
 def attn_output(kvz, wl, data, scale, stream):
@@ -616,6 +675,8 @@ def main():
     if not args.no_extras:
         out["decode"] = decode_sweep(kvz, wl, S, kc_flat, vc_flat)
         log("decode sweep done")
+        out["structured_eviction"] = structured_evictions(kvz, wl, S, kc_flat, vc_flat)
+        log("head-level and token-level evictions done")
         out["attn_output"] = attn_output(kvz, wl, data, scale, stream)
         log("attention-output call done")
     if args.copy_calibration:

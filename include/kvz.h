@@ -192,6 +192,45 @@ KVZ_API kvz_status kvz_token_scores(const float* S, int64_t n_heads, int n_c, fl
                                     void* stream);
 
 /* ------------------------------------------------------------------------
+ * Structured evictions on the same scores, each producing the mask and head
+ * offsets that kvz_compact consumes (same layout as kvz_select_threshold's).
+ *
+ * kvz_select_heads -- context-independent head-level eviction (rebuttal,
+ * answer on how head-level scores were computed: a head's score is the max
+ * of S along the sequence axis; blog 5.4: KVzip's scores drive head-level
+ * eviction in place of DuoAttention's).  The K_heads heads with the highest
+ * head scores keep every token (exactly K_heads; ties to the lower flat head
+ * index); every other head keeps its first n_sink and its last n_recent
+ * tokens (the streaming-head structure of DuoAttention: the pages do not say
+ * what an evicted head keeps).
+ *   S            device fp32 [n_heads][n_c], 16-byte aligned, no NaN.
+ *   mask         device uint8 [n_heads * n_c], 16-byte aligned, out.
+ *   head_offsets device int64 [n_heads + 1], out (exclusive scan of the
+ *                per-head kept counts).
+ *   head_keep    device uint8 [n_heads], out: 1 = head kept whole.
+ * 0 <= K_heads <= n_heads, n_sink >= 0, n_recent >= 0, n_heads * n_c < 2^31.
+ * Workspace: kvz_select_heads_workspace() bytes, 256-byte aligned.
+ *
+ * kvz_select_tokens -- token-level eviction (blog 4.3.3: one score per
+ * token, the max over all layers and heads; sorting those decides which
+ * tokens stay).  The K_tokens positions with the highest token scores
+ * (exactly K_tokens; ties to the lower position) are kept in every head, so
+ * head_offsets[h] = h * K_tokens.
+ *   token_keep   device uint8 [n_c], out: 1 = position kept.
+ * 0 <= K_tokens <= n_c; the other arguments as for kvz_select_heads.
+ * Workspace: kvz_select_tokens_workspace() bytes, 256-byte aligned.
+ * ---------------------------------------------------------------------- */
+KVZ_API size_t kvz_select_heads_workspace(int64_t n_heads, int n_c);
+KVZ_API kvz_status kvz_select_heads(const float* S, int64_t n_heads, int n_c, int64_t K_heads,
+                                    int n_sink, int n_recent, uint8_t* mask,
+                                    int64_t* head_offsets, uint8_t* head_keep, void* ws,
+                                    size_t ws_bytes, void* stream);
+KVZ_API size_t kvz_select_tokens_workspace(int64_t n_heads, int n_c);
+KVZ_API kvz_status kvz_select_tokens(const float* S, int64_t n_heads, int n_c, int64_t K_tokens,
+                                     uint8_t* mask, int64_t* head_offsets, uint8_t* token_keep,
+                                     void* ws, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
  * Keep count K = r * N rounded half up, clamped to [0, N] (host only).
  * ---------------------------------------------------------------------- */
 KVZ_API int64_t kvz_keep_count(int64_t N, double r);
@@ -279,7 +318,8 @@ KVZ_API kvz_status kvz_decode_packed(kvz_dtype dt, int64_t n_heads, int G, int d
  * HIP events on its stream.  kvz_prof_read() synchronises those events and
  * returns, for the kernel named `name` ("score_pass1", "score_combine",
  * "score_pass2", "attn_pass3", "attn_reduce", "select_*", "compact_*",
- * "head_scores", "token_scores", "decode_split", "decode_combine"), the
+ * "head_scores", "token_scores", "evict_mask", "evict_offsets",
+ * "decode_split", "decode_combine"), the
  * number of launches and the
  * summed duration in milliseconds since the last enable.  Returns KVZ_OK, or
  * KVZ_ERR_INVALID_ARG for an unknown name.  max_launches bounds the event

@@ -358,3 +358,48 @@ def test_noalloc_scratch_covers_the_workloads():
     assert kvz.kvz_score_chunk_workspace(kvz.KVZ_BF16, 4, 64, 8192, 128, 1000) > cap
     hdr = open(os.path.join(ROOT, "include", "kvz.h")).read()
     assert re.search(r"#define KVZ_NOALLOC_SCRATCH_BYTES \(16u << 20\)", hdr)
+
+
+def test_structured_select_validation():
+    L = kvz.lib()
+    fh = lambda S=FAKE, nh=4, nc=10, K=2, s=1, r=1, m=FAKE, o=FAKE, k=FAKE, ws=FAKE, wsb=1 << 30: \
+        L.kvz_select_heads(S, nh, nc, K, s, r, m, o, k, ws, wsb, None)
+    assert fh(K=5) == kvz.KVZ_ERR_INVALID_ARG
+    assert fh(K=-1) == kvz.KVZ_ERR_INVALID_ARG
+    assert fh(s=-1) == kvz.KVZ_ERR_INVALID_ARG
+    assert fh(r=-2) == kvz.KVZ_ERR_INVALID_ARG
+    assert fh(nh=0) == kvz.KVZ_ERR_INVALID_ARG
+    assert fh(S=None) == kvz.KVZ_ERR_INVALID_ARG
+    assert fh(k=None) == kvz.KVZ_ERR_INVALID_ARG
+    assert fh(m=P(4097)) == kvz.KVZ_ERR_INVALID_ARG      # mask must be 16-byte aligned
+    assert fh(o=P(4100)) == kvz.KVZ_ERR_INVALID_ARG
+    assert fh(wsb=8) == kvz.KVZ_ERR_WORKSPACE
+    assert fh(nh=1 << 20, nc=1 << 12) == kvz.KVZ_ERR_INVALID_ARG
+    ft = lambda S=FAKE, nh=4, nc=10, K=3, m=FAKE, o=FAKE, k=FAKE, ws=FAKE, wsb=1 << 30: \
+        L.kvz_select_tokens(S, nh, nc, K, m, o, k, ws, wsb, None)
+    assert ft(K=11) == kvz.KVZ_ERR_INVALID_ARG
+    assert ft(K=-1) == kvz.KVZ_ERR_INVALID_ARG
+    assert ft(S=MIS) == kvz.KVZ_ERR_INVALID_ARG
+    assert ft(k=None) == kvz.KVZ_ERR_INVALID_ARG
+    assert ft(ws=P(4096 + 128)) == kvz.KVZ_ERR_INVALID_ARG
+    assert ft(wsb=8) == kvz.KVZ_ERR_WORKSPACE
+    assert kvz.kvz_select_heads_workspace(256, 131072) > 0
+    assert kvz.kvz_select_tokens_workspace(256, 131072) > 0
+    assert kvz.kvz_select_heads_workspace(0, 10) == 0
+    assert kvz.kvz_select_tokens_workspace(1 << 20, 1 << 12) == 0
+
+
+@pytest.mark.parametrize("fn", ["heads", "tokens"])
+def test_structured_select_binding_rejects(fn):
+    S = torch.zeros(4, 10)
+    f = (lambda **kw: kvz.kvz_select_heads(S, 2, 1, 1, **kw)) if fn == "heads" else \
+        (lambda **kw: kvz.kvz_select_tokens(S, 3, **kw))
+    keep_n = 4 if fn == "heads" else 10
+    keep_name = "head_keep" if fn == "heads" else "token_keep"
+    for kw, name in ((dict(mask=_t(39, torch.uint8)), "mask"),
+                     (dict(head_offsets=_t(5, torch.int32)), "head_offsets"),
+                     ({keep_name: _t(keep_n - 1, torch.uint8)}, keep_name),
+                     ({keep_name: _t(keep_n, torch.int8)}, keep_name)):
+        with pytest.raises((TypeError, ValueError), match=name) as e:
+            f(**kw)
+        assert "device tensor" not in str(e.value)
