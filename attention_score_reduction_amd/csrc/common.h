@@ -87,6 +87,7 @@ hipError_t score_launch(kvz_dtype dt, kvz_aggregate agg, const ScorePlan& p, con
                         const void* kc, const void* kin, float scale, float* S, void* ws,
                         hipStream_t st);
 
+
 // reconstruction attention output (after the score passes of the same call,
 // reusing their row log-sum-exp from the score workspace)
 struct AttnPlan {

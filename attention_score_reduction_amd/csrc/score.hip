@@ -151,46 +151,77 @@ struct P1Shape {
   static constexpr int ROWS = 4 * 32 * NQ;                     // query rows per workgroup
 };
 
+// arguments of one pass-1 launch (one chunk, all heads)
+struct P1Args {
+  const uint16_t* q;     // [H][G][n_in][d]
+  const uint16_t* kc;    // [H][n_c][d]
+  const uint16_t* kin;   // [H][n_in][d]
+  float2* part;          // [H][splits][R_pad] partial (max, sum), g-major rows
+  int G, n_c, n_in, R, R_pad, n_rt, n_split_ctx, tiles_per_split;
+  float cl2;
+  int n_blocks;          // H * splits * n_rt
+};
+
+// key tiles of pass-1 item lb: [t_begin, t_clean) run the pipelined loop,
+// [t_clean, t_end) the masked path (the ragged last context tile).  The
+// context splits cover tiles_per_split 32-key tiles of the n_c context keys;
+// the in-chunk split covers the causal chunk keys up to the last row of the
+// item's row tile.
+struct P1Range {
+  int t_begin, t_end, t_clean;
+};
+
 template <int D>
-__global__ __launch_bounds__(256) void score_pass1_bf16(
-    const uint16_t* __restrict__ q, const uint16_t* __restrict__ kc,
-    const uint16_t* __restrict__ kin, float2* __restrict__ part, int G, int n_c, int n_in,
-    int R, int R_pad, int n_rt, int n_split_ctx, int tiles_per_split, float cl2,
-    int n_blocks) {
+__device__ __forceinline__ P1Range p1_range(const P1Args& a, int lb) {
+  const int splits = a.n_split_ctx + 1;
+  const int rt = lb % a.n_rt;
+  const int s = (lb / a.n_rt) % splits;
+  P1Range r;
+  if (s != a.n_split_ctx) {
+    const int n_tiles_ctx = (a.n_c + KT - 1) / KT;
+    r.t_begin = s * a.tiles_per_split;
+    r.t_end = min(n_tiles_ctx, r.t_begin + a.tiles_per_split);
+    r.t_clean = (r.t_end == n_tiles_ctx && (a.n_c % KT) != 0) ? r.t_end - 1 : r.t_end;
+  } else {
+    const int rlast = min(a.R, (rt + 1) * P1Shape<D>::ROWS) - 1;
+    r.t_begin = 0;
+    r.t_end = (rlast / a.G) / KT + 1;
+    r.t_clean = r.t_end;  // pipelined, causal mask in the accumulator start
+  }
+  return r;
+}
+
+// one pass-1 workgroup item lb (head, key split, row tile), run by 256
+// threads whose local index is tid
+template <int D>
+__device__ __forceinline__ void p1_block(const P1Args& args, int lb, int tid) {
   constexpr int KS = Geo<D>::KS, CH = Geo<D>::CH, SWZ = Geo<D>::SWZ;
   constexpr int NQ = P1Shape<D>::NQ, ROWS = P1Shape<D>::ROWS;
   constexpr int LOADS = KT * CH / 256;
   constexpr int AW = KS <= 8 ? KS : 4;  // A-operand k-steps held at once
   __shared__ uint4 lds0[KT * CH], lds1[KT * CH];
 
-  const int lb = xcd_logical_block();
-  if (lb >= n_blocks) return;
+  const uint16_t* __restrict__ q = args.q;
+  const uint16_t* __restrict__ kc = args.kc;
+  const uint16_t* __restrict__ kin = args.kin;
+  float2* __restrict__ part = args.part;
+  const int G = args.G, n_c = args.n_c, n_in = args.n_in, R = args.R, R_pad = args.R_pad;
+  const int n_rt = args.n_rt, n_split_ctx = args.n_split_ctx;
+  const int tiles_per_split = args.tiles_per_split;
+  const float cl2 = args.cl2;
   const int splits = n_split_ctx + 1;
   const int rt = lb % n_rt;
   const int s = (lb / n_rt) % splits;
   const int h = lb / (n_rt * splits);
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63, wave = tid >> 6;
   const int n = lane & 31, half = lane >> 5;
 
   const bool inchunk = (s == n_split_ctx);
-  const int n_tiles_ctx = (n_c + KT - 1) / KT;
-  const uint16_t* kbase;
-  int nkeys, t_begin, t_end, t_clean;
-  if (!inchunk) {
-    kbase = kc + (size_t)h * n_c * D;
-    nkeys = n_c;
-    t_begin = s * tiles_per_split;
-    t_end = min(n_tiles_ctx, t_begin + tiles_per_split);
-    t_clean = (t_end == n_tiles_ctx && (n_c % KT) != 0) ? t_end - 1 : t_end;
-  } else {
-    kbase = kin + (size_t)h * n_in * D;
-    nkeys = n_in;
-    const int rlast = min(R, (rt + 1) * ROWS) - 1;
-    t_begin = 0;
-    t_end = (rlast / G) / KT + 1;
-    t_clean = t_end;  // pipelined, causal mask in the accumulator start
-  }
+  const P1Range rg = p1_range<D>(args, lb);
+  const int t_begin = rg.t_begin, t_end = rg.t_end, t_clean = rg.t_clean;
+  const uint16_t* kbase = inchunk ? kin + (size_t)h * n_in * D : kc + (size_t)h * n_c * D;
+  const int nkeys = inchunk ? n_in : n_c;
 
   // stationary query operand (B of K*Q^T): this lane's query column n of
   // each of the wave's NQ row tiles
@@ -435,6 +466,13 @@ __global__ __launch_bounds__(256) void score_pass1_bf16(
   }
 }
 
+template <int D>
+__global__ __launch_bounds__(256) void score_pass1_bf16(P1Args args) {
+  const int lb = xcd_logical_block();
+  if (lb >= args.n_blocks) return;
+  p1_block<D>(args, lb, threadIdx.x);
+}
+
 // merge the key splits: lse2 = M + log2(sum_s l_s 2^(m_s - M)), written
 // times mul (1, or -1/(scale log2 e) when pass 2 takes it in raw dot-product
 // units); padding rows get +inf * mul so that pass 2 ignores them.
@@ -482,13 +520,22 @@ struct P2Shape {
   static constexpr int KEYS = 4 * 32 * NT;       // keys per workgroup
 };
 
-template <int D, int MODE>
-__global__ __launch_bounds__(256) void score_pass2_bf16(
-    const uint16_t* __restrict__ q, const uint16_t* __restrict__ kc,
-    const float* __restrict__ lse2, float* __restrict__ S, int G, int n_c, int n_in, int R,
-    int R_pad, int n_kt, float cl2, float scale, int n_blocks) {
+// arguments of one pass-2 launch (one chunk, all heads)
+struct P2Args {
+  const uint16_t* q;     // [H][G][n_in][d]
+  const uint16_t* kc;    // [H][n_c][d]
+  const float* lse2;     // [H][R_pad] row log-sum-exp (or its pass-2 form)
+  float* S;              // [H][n_c]
+  int G, n_c, n_in, R, R_pad, n_kt;
+  float cl2, scale;
+  int n_blocks;          // H * n_kt
+};
+
+// one pass-2 workgroup item lb (head, block of 4 * 32 * NT keys), run by 256
+// threads whose local index is tid
+template <int D, int MODE, int NT>
+__device__ __forceinline__ void p2_block(const P2Args& args, int lb, int tid) {
   constexpr int KS = Geo<D>::KS, CH = Geo<D>::CH, SWZ = Geo<D>::SWZ;
-  constexpr int NT = P2Shape<D>::NT;
   constexpr int RT = 32;                     // query rows per tile
   constexpr int LOADS = RT * CH / 256;       // 16-byte copies per thread per tile
   __shared__ uint4 ldq[2][RT * CH];
@@ -496,13 +543,17 @@ __global__ __launch_bounds__(256) void score_pass2_bf16(
   // copying wave, although only 8 lanes copy
   __shared__ float4 ldl[2][64];
 
-  const int lb = xcd_logical_block();
-  if (lb >= n_blocks) return;
+  const uint16_t* __restrict__ q = args.q;
+  const uint16_t* __restrict__ kc = args.kc;
+  const float* __restrict__ lse2 = args.lse2;
+  float* __restrict__ S = args.S;
+  const int n_c = args.n_c, R = args.R, R_pad = args.R_pad, n_kt = args.n_kt;
+  const float cl2 = args.cl2, scale = args.scale;
   const int kt = lb % n_kt;
   const int h = lb / n_kt;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63, wave = tid >> 6;
   const int n = lane & 31, half = lane >> 5;
-  const int j0 = kt * P2Shape<D>::KEYS + wave * (32 * NT);
+  const int j0 = kt * (4 * 32 * NT) + wave * (32 * NT);
 
   // stationary key operand (B of Q*K^T): this lane's key column n of each
   // tile; keys past n_c re-read key n_c - 1 and are never written back
@@ -634,6 +685,13 @@ __global__ __launch_bounds__(256) void score_pass2_bf16(
   }
 }
 
+template <int D, int MODE>
+__global__ __launch_bounds__(256) void score_pass2_bf16(P2Args args) {
+  const int lb = xcd_logical_block();
+  if (lb >= args.n_blocks) return;
+  p2_block<D, MODE, P2Shape<D>::NT>(args, lb, threadIdx.x);
+}
+
 // ---------------------------------------------------------------------------
 // fp32 path (VALU): one thread per query row (pass 1) / per context key (pass 2)
 // ---------------------------------------------------------------------------
@@ -735,18 +793,19 @@ hipError_t launch_bf16(const ScorePlan& p, const void* q, const void* kc, const 
   const int splits = p.n_split_ctx + 1;
   if (MODE != 2) {
     const int nb1 = p.H * splits * p.n_rt;
-    KVZ_LAUNCH("score_pass1", score_pass1_bf16<D>, xcd_padded_grid(nb1), 256, 0, st,
-               (const uint16_t*)q, (const uint16_t*)kc, (const uint16_t*)kin, part, p.G, p.n_c,
-               p.n_in, p.R, p.R_pad, p.n_rt, p.n_split_ctx, p.tiles_per_split, cl2, nb1);
+    const P1Args a1{(const uint16_t*)q, (const uint16_t*)kc, (const uint16_t*)kin, part, p.G,
+                    p.n_c, p.n_in, p.R, p.R_pad, p.n_rt, p.n_split_ctx, p.tiles_per_split, cl2,
+                    nb1};
+    KVZ_LAUNCH("score_pass1", score_pass1_bf16<D>, xcd_padded_grid(nb1), 256, 0, st, a1);
     const int nc = p.H * p.R_pad;
     KVZ_LAUNCH("score_combine", score_combine, (nc + 255) / 256, 256, 0, st, part, lse2, splits,
                p.R, p.R_pad, p.H, MODE == 0 ? -1.0f / cl2 : 1.0f);
   }
   const int n_kt = (p.n_c + P2Shape<D>::KEYS - 1) / P2Shape<D>::KEYS;
   const int nb2 = p.H * n_kt;
-  KVZ_LAUNCH("score_pass2", (score_pass2_bf16<D, MODE>), xcd_padded_grid(nb2), 256, 0, st,
-             (const uint16_t*)q, (const uint16_t*)kc, lse2, S, p.G, p.n_c, p.n_in, p.R,
-             p.R_pad, n_kt, cl2, scale, nb2);
+  const P2Args a2{(const uint16_t*)q, (const uint16_t*)kc, lse2, S, p.G, p.n_c, p.n_in, p.R,
+                  p.R_pad, n_kt, cl2, scale, nb2};
+  KVZ_LAUNCH("score_pass2", (score_pass2_bf16<D, MODE>), xcd_padded_grid(nb2), 256, 0, st, a2);
   return hipGetLastError();
 }
 
