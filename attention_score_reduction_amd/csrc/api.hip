@@ -46,7 +46,7 @@ void prof_before(const char* name, hipStream_t s) {
 void prof_after(hipStream_t s) {
   Prof& p = prof();
   if (p.pending < 0) return;
-  hipEventRecord(p.recs[p.pending].b, s);
+  (void)hipEventRecord(p.recs[p.pending].b, s);
   p.pending = -1;
 }
 
@@ -64,7 +64,7 @@ bool head_dim_ok(int d) { return d == 64 || d == 128 || d == 256; }
 bool ctx_fits(int n_c, int d) {
   return n_c <= (1 << 24) && (long long)n_c * d * 2 <= 0x7fffffffLL;
 }
-hipError_t clear_error() { return hipGetLastError(); }
+void clear_error() { (void)hipGetLastError(); }
 
 }  // namespace
 
@@ -152,8 +152,13 @@ kvz_status kvz_score_chunk_attn(kvz_dtype dt, int H, int G, int d, int n_c, int 
   if (ws_bytes < p.total_bytes + a.part_bytes) return KVZ_ERR_WORKSPACE;
   clear_error();
   const hipStream_t st = reinterpret_cast<hipStream_t>(stream);
-  hipError_t e = score_launch(dt, KVZ_AGG_MAX, p, q, k_ctx, k_in, scale, S, ws, st);
-  if (e == hipSuccess) e = attn_launch(dt, p, a, q, k_ctx, k_in, v_ctx, v_in, scale, O, ws, st);
+  // bf16: the output pass forms the rows' (max, sum) partials itself and the
+  // score update runs from them; fp32: the score passes first, then the
+  // output from their row log-sum-exp
+  hipError_t e = hipSuccess;
+  if (dt == KVZ_F32) e = score_launch(dt, KVZ_AGG_MAX, p, q, k_ctx, k_in, scale, S, ws, st);
+  if (e == hipSuccess)
+    e = attn_launch(dt, p, a, q, k_ctx, k_in, v_ctx, v_in, scale, S, O, ws, st);
   return e == hipSuccess ? KVZ_OK : KVZ_ERR_HIP;
 }
 
@@ -318,7 +323,7 @@ kvz_status kvz_decode_packed(kvz_dtype dt, int64_t n_heads, int G, int d, int ma
 
 kvz_status kvz_prof_enable(int on, int max_launches) {
   Prof& p = prof();
-  for (hipEvent_t e : p.pool) hipEventDestroy(e);
+  for (hipEvent_t e : p.pool) (void)hipEventDestroy(e);
   p.pool.clear();
   p.recs.clear();
   p.on = false;

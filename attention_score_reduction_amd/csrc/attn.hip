@@ -7,19 +7,25 @@
 //     O[h][g][i] = sum over visible keys j of p_ij * v_j,
 // v_j the rows of [V_c; V_in], p the same softmax rows the scores come from
 // (KVzip blog post, section 4.4: a FlashAttention kernel returns exactly this
-// product).  It runs after the score passes of the same call and reuses their
-// row log-sum-exp, so every p_ij is final when it is formed: no running
-// rescale, and the key axis splits over workgroups whose partial outputs
-// simply add.
+// product, and not the max over rows of p that the scores need).
 //
-// bf16 path: rows stationary, keys swept (the K*Q^T orientation of score
-// pass 1); per 32-key tile one wave computes its 32 rows' logits on MFMA with
-// the accumulator started at the row's -lse2/(scale log2 e), so
-// p = 2^(scale log2 e * acc); p is rounded to bf16 and, still in the
-// accumulator layout, is the B operand of O^T += V^T P.  V tiles stay
-// row-major in LDS; the A operand (keys contiguous per d index, in the key
-// order that layout implies) comes from transposing LDS reads.  fp32 path: a
-// plain VALU kernel for small fp32 problems.
+// bf16 path, three kernels: (1) the output pass sweeps every visible key of
+// each query row once, forming the row's unnormalised output and its running
+// (max, sum) per key split, with a lazily moved max as in score pass 1;
+// (2) the split merge of those (max, sum) pairs gives the row log-sum-exp and
+// score pass 2 forms the scores from it (score.hip); (3) the output merge
+// rescales each split's output by 2^(m_split - M) / L.  So the logits are
+// formed twice per call (here and in score pass 2), not three times.
+//
+// Output pass: rows stationary, keys swept (the K*Q^T orientation of score
+// pass 1); per 32-key tile one wave computes its 32 rows' logits on MFMA;
+// p = 2^(scale log2 e * x - m) is rounded to bf16 and, still in the
+// accumulator layout, is the B operand of O^T += V^T P.  The two lanes that
+// hold the same query column share m, so their P values in one MFMA carry
+// the same scale.  V tiles stay row-major in LDS; the A operand (keys
+// contiguous per d index, in the key order that layout implies) comes from
+// transposing LDS reads.  fp32 path: a plain VALU kernel for small fp32
+// problems, after the fp32 score passes.
 #include "common.h"
 
 namespace kvz {
@@ -28,9 +34,13 @@ namespace {
 
 constexpr int KT = 32;      // keys per tile
 constexpr int ROWS3 = 128;  // query rows per workgroup (4 waves x 32)
+constexpr float kNegBig3 = -1e30f;
+// the running max of a row moves only when a tile's terms against it sum
+// past 2^30 (every term then stays below 2^30 times the row's max term)
+constexpr float kLazyLimit3 = 1073741824.f;
 
 #ifndef KVZ_ATTN_TARGET_WGS
-#define KVZ_ATTN_TARGET_WGS 2048  // workgroups aimed for per call (sets the key splits)
+#define KVZ_ATTN_TARGET_WGS 4096  // workgroups aimed for per call (sets the key splits)
 #endif
 
 template <int D>
@@ -60,8 +70,10 @@ __device__ __forceinline__ v4i16 lds_read_tr4(const void* p) {
 }
 
 // grid: H x splits x row tiles (XCD-remapped, head-major); rows i-major
-// (r = i*G + g).  nlse: [H][R_pad] g-major, -lse2/(scale log2 e) (padding
-// rows -inf).  opart: [splits][H][R_pad][D] fp32, rows i-major.
+// (r = i*G + g).  opart: [splits][H][R_pad][D] fp32, rows i-major, each
+// split's output unnormalised against its running max; mlpart:
+// [H][splits][R_pad] (max, sum) of each (row, split), g-major rows, log2
+// units of the scaled logits (the layout score pass 1 writes).
 //
 // K and V tiles (32 keys each) go global -> LDS by buffer loads with an LDS
 // destination, row-major: K with 16-byte chunks XOR-swizzled by the key
@@ -76,10 +88,10 @@ __device__ __forceinline__ v4i16 lds_read_tr4(const void* p) {
 // the tile).  The block swizzle puts a group's four keys in four different
 // 32-byte blocks of the bank space.
 template <int D>
-__global__ __launch_bounds__(256) void attn_pass3_bf16(
+__global__ __launch_bounds__(256) void attn_flash_bf16(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ kc,
     const uint16_t* __restrict__ kin, const uint16_t* __restrict__ vc,
-    const uint16_t* __restrict__ vin, const float* __restrict__ nlse, float* __restrict__ opart,
+    const uint16_t* __restrict__ vin, float* __restrict__ opart, float2* __restrict__ mlpart,
     int H, int G, int n_c, int n_in, int R, int R_pad, int n_rt, int n_split_ctx,
     int tiles_per_split, float cl2, int n_blocks) {
   constexpr int KS = G3<D>::KS, CH = G3<D>::CH, SWZ = G3<D>::SWZ, DT = G3<D>::DT;
@@ -121,16 +133,17 @@ __global__ __launch_bounds__(256) void attn_pass3_bf16(
   const int r = rt * ROWS3 + wave * 32 + n;
   const int irow = r / G, grow = r - irow * G;
   bf16x8 qr[KS];
-  float start = -INFINITY;
   if (r < R) {
     const uint16_t* p = q + ((size_t)(h * G + grow) * n_in + irow) * D + half * 8;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) qr[ks] = as_bf16x8(ld16(p + ks * 16));
-    start = nlse[(size_t)h * R_pad + grow * n_in + irow];
   } else {
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) qr[ks] = as_bf16x8(make_uint4(0, 0, 0, 0));
   }
+  // running max of the row (log2 units, shared by the lanes n and n + 32 of
+  // the query column) and this lane's share of the sum against it
+  float m = kNegBig3, l = 0.f;
 
   f32x16 o[DT];
 #pragma unroll
@@ -168,19 +181,17 @@ __global__ __launch_bounds__(256) void attn_pass3_bf16(
   for (int dt = 0; dt < DT; ++dt)
     vrd[dt] = tr_key * D * 2 + (((2 * dt + tr_mh) ^ (((tr_key & 3) << 1) & VSW)) * 32) + tr_a * 8;
 
-  // accumulator start of a tile's logits: the row's offset, or -inf on keys
-  // the row does not see (only the ragged context tile and the chunk tiles)
-  f32x16 cst;
-#pragma unroll
-  for (int v = 0; v < 16; ++v) cst[v] = start;
+  // accumulator start of a tile's logits: 0, or -inf on keys the row does
+  // not see (only the ragged context tile and the chunk tiles)
+  const f32x16 zero = {};
   auto init_of = [&](int tile) -> f32x16 {
-    if (!inchunk && (tile + 1) * KT <= n_c) return cst;
+    if (!inchunk && (tile + 1) * KT <= n_c) return zero;
     f32x16 z;
 #pragma unroll
     for (int v = 0; v < 16; ++v) {
       const int key = tile * KT + acc_row3(v, half);
       const bool vis = inchunk ? key <= irow : key < n_c;
-      z[v] = vis ? start : -INFINITY;
+      z[v] = vis ? 0.f : -INFINITY;
     }
     return z;
   };
@@ -207,10 +218,38 @@ __global__ __launch_bounds__(256) void attn_pass3_bf16(
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
 #pragma unroll
-      for (int v = ks * 16 / KS; v < (ks + 1) * 16 / KS; ++v) p[v] = fast_exp2(cur[v] * cl2);
+      for (int v = ks * 16 / KS; v < (ks + 1) * 16 / KS; ++v)
+        p[v] = fast_exp2(fmaf(cur[v], cl2, -m));
       nxt = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[ks], qr[ks], ks == 0 ? init : nxt, 0, 0, 0);
       __builtin_amdgcn_sched_barrier(0);
     }
+    // lazy commit: the max of a query column moves only when one of its two
+    // lanes sums this tile's terms past half the limit (so the column's sum
+    // stays below the limit); then the whole wave (a uniform branch) raises
+    // each column's max to its tile max, rescales the output and sum so far,
+    // and forms the terms again (always on the first tile, whose max starts
+    // at -1e30)
+    float ts = ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7])) +
+               (((p[8] + p[9]) + (p[10] + p[11])) + ((p[12] + p[13]) + (p[14] + p[15])));
+    if (__ballot(!(ts <= 0.5f * kLazyLimit3))) {
+      float mx = cur[0];
+#pragma unroll
+      for (int v = 1; v < 16; ++v) mx = fmaxf(mx, cur[v]);
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      const float mn = fmaxf(m, mx * cl2);
+      const float alpha = fast_exp2(m - mn);
+      l *= alpha;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) o[dt][v] *= alpha;
+      m = mn;
+#pragma unroll
+      for (int v = 0; v < 16; ++v) p[v] = fast_exp2(fmaf(cur[v], cl2, -m));
+      ts = ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7])) +
+           (((p[8] + p[9]) + (p[10] + p[11])) + ((p[12] + p[13]) + (p[14] + p[15])));
+    }
+    l += ts;
     bf16x8 pb[2];
 #pragma unroll
     for (int qq = 0; qq < 2; ++qq)
@@ -256,6 +295,10 @@ __global__ __launch_bounds__(256) void attn_pass3_bf16(
     if (tile < t_end) body(tile, 0, A, B);
   }
 
+  // the two lanes of a query column share m: their sums add
+  const float lcol = l + __shfl_xor(l, 32);
+  if (half == 0 && r < R)
+    mlpart[((size_t)h * splits + s) * R_pad + grow * n_in + irow] = make_float2(m, lcol);
   // lane (n, half) holds d = 32 dt + 8 vg + 4 half + 0..3 of query row r
   float* op = opart + (((size_t)s * H + h) * R_pad + r) * D;
 #pragma unroll
@@ -266,9 +309,11 @@ __global__ __launch_bounds__(256) void attn_pass3_bf16(
           make_float4(o[dt][4 * vg], o[dt][4 * vg + 1], o[dt][4 * vg + 2], o[dt][4 * vg + 3]);
 }
 
-// O[h][g][i][:] = sum over splits of opart[s][h][i*G + g][:]
+// O[h][g][i][:] = sum over splits s of opart[s][h][i*G + g][:] * 2^(m_s - M) / L,
+// M the max of the splits' maxima m_s and L = sum of l_s 2^(m_s - M)
 template <int D>
 __global__ __launch_bounds__(256) void attn_reduce(const float* __restrict__ opart,
+                                                   const float2* __restrict__ mlpart,
                                                    float* __restrict__ O, int H, int G, int n_in,
                                                    int R_pad, int splits) {
   const long long idx = (long long)blockIdx.x * 256 + threadIdx.x;  // one float4
@@ -280,16 +325,25 @@ __global__ __launch_bounds__(256) void attn_reduce(const float* __restrict__ opa
   const int hg = (int)(row / n_in);
   const int h = hg / G, g = hg - h * G;
   const int r = i * G + g;
+  const float2* ml = mlpart + (size_t)h * splits * R_pad + g * n_in + i;
+  float M = kNegBig3;
+  for (int s = 0; s < splits; ++s) M = fmaxf(M, ml[(size_t)s * R_pad].x);
+  float L = 0.f;
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
   for (int s = 0; s < splits; ++s) {
+    const float2 v2 = ml[(size_t)s * R_pad];
+    const float w = fast_exp2(v2.x - M);
+    L += v2.y * w;
     const float4 v =
         *reinterpret_cast<const float4*>(opart + (((size_t)s * H + h) * R_pad + r) * D + 4 * c4);
-    acc.x += v.x;
-    acc.y += v.y;
-    acc.z += v.z;
-    acc.w += v.w;
+    acc.x += w * v.x;
+    acc.y += w * v.y;
+    acc.z += w * v.z;
+    acc.w += w * v.w;
   }
-  *reinterpret_cast<float4*>(O + row * D + 4 * c4) = acc;
+  const float inv = 1.0f / L;
+  *reinterpret_cast<float4*>(O + row * D + 4 * c4) =
+      make_float4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv);
 }
 
 // fp32: one workgroup of 64 threads per query row; 64 keys at a time, one
@@ -350,20 +404,25 @@ __global__ __launch_bounds__(64) void attn_f32(const float* __restrict__ q,
 template <int D>
 hipError_t launch3(kvz_dtype dt, const ScorePlan& p, const AttnPlan& a, const void* q,
                    const void* kc, const void* kin, const void* vc, const void* vin, float scale,
-                   float* O, void* ws, hipStream_t st) {
+                   float* S, float* O, void* ws, hipStream_t st) {
   const float cl2 = scale * 1.4426950408889634f;
   if (dt == KVZ_BF16) {
-    const float* nlse = reinterpret_cast<const float*>(reinterpret_cast<char*>(ws) + p.part_bytes);
     float* opart = reinterpret_cast<float*>(reinterpret_cast<char*>(ws) + p.total_bytes);
+    float2* mlpart = reinterpret_cast<float2*>(reinterpret_cast<char*>(ws) + p.total_bytes +
+                                               a.opart_bytes);
     const int splits = a.n_split_ctx + 1;
     const int nb = p.H * splits * a.n_rt;
-    KVZ_LAUNCH("attn_pass3", attn_pass3_bf16<D>, xcd_padded_grid(nb), 256, 0, st,
+    KVZ_LAUNCH("attn_pass3", attn_flash_bf16<D>, xcd_padded_grid(nb), 256, 0, st,
                (const uint16_t*)q, (const uint16_t*)kc, (const uint16_t*)kin,
-               (const uint16_t*)vc, (const uint16_t*)vin, nlse, opart, p.H, p.G, p.n_c, p.n_in,
+               (const uint16_t*)vc, (const uint16_t*)vin, opart, mlpart, p.H, p.G, p.n_c, p.n_in,
                p.R, p.R_pad, a.n_rt, a.n_split_ctx, a.tiles_per_split, cl2, nb);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    e = score_finish_launch(p, mlpart, splits, q, kc, scale, S, ws, st);
+    if (e != hipSuccess) return e;
     const long long total = (long long)p.H * p.G * p.n_in * (D / 4);
     KVZ_LAUNCH("attn_reduce", attn_reduce<D>, (unsigned)((total + 255) / 256), 256, 0, st, opart,
-               O, p.H, p.G, p.n_in, p.R_pad, splits);
+               mlpart, O, p.H, p.G, p.n_in, p.R_pad, splits);
   } else {
     const float* lse2 = reinterpret_cast<const float*>(ws);
     dim3 grid(p.R, p.H);
@@ -388,18 +447,20 @@ AttnPlan attn_plan(kvz_dtype dt, const ScorePlan& p) {
   if (want < 1) want = 1;
   a.tiles_per_split = (n_ctx_tiles + want - 1) / want;
   a.n_split_ctx = (n_ctx_tiles + a.tiles_per_split - 1) / a.tiles_per_split;
-  a.part_bytes =
+  a.opart_bytes =
       align256((size_t)(a.n_split_ctx + 1) * p.H * p.R_pad * p.d * sizeof(float));
+  a.part_bytes =
+      a.opart_bytes + align256((size_t)(a.n_split_ctx + 1) * p.H * p.R_pad * sizeof(float2));
   return a;
 }
 
 hipError_t attn_launch(kvz_dtype dt, const ScorePlan& p, const AttnPlan& a, const void* q,
                        const void* kc, const void* kin, const void* vc, const void* vin,
-                       float scale, float* O, void* ws, hipStream_t st) {
+                       float scale, float* S, float* O, void* ws, hipStream_t st) {
   switch (p.d) {
-    case 64: return launch3<64>(dt, p, a, q, kc, kin, vc, vin, scale, O, ws, st);
-    case 128: return launch3<128>(dt, p, a, q, kc, kin, vc, vin, scale, O, ws, st);
-    case 256: return launch3<256>(dt, p, a, q, kc, kin, vc, vin, scale, O, ws, st);
+    case 64: return launch3<64>(dt, p, a, q, kc, kin, vc, vin, scale, S, O, ws, st);
+    case 128: return launch3<128>(dt, p, a, q, kc, kin, vc, vin, scale, S, O, ws, st);
+    case 256: return launch3<256>(dt, p, a, q, kc, kin, vc, vin, scale, S, O, ws, st);
   }
   return hipErrorInvalidValue;
 }

@@ -86,6 +86,11 @@ ScorePlan score_plan(kvz_dtype dt, int H, int G, int n_in, int d, int n_c);
 hipError_t score_launch(kvz_dtype dt, kvz_aggregate agg, const ScorePlan& p, const void* q,
                         const void* kc, const void* kin, float scale, float* S, void* ws,
                         hipStream_t st);
+// bf16 score update from per-split row (max, sum) partials part[H][splits][R_pad]
+// (g-major rows, log2 units of the scaled logits): split merge into the
+// score workspace's row offsets, then pass 2 into S
+hipError_t score_finish_launch(const ScorePlan& p, const float2* part, int splits, const void* q,
+                               const void* kc, float scale, float* S, void* ws, hipStream_t st);
 
 
 // reconstruction attention output (after the score passes of the same call,
@@ -94,12 +99,17 @@ struct AttnPlan {
   int n_rt;             // row tiles of 128 rows per head
   int n_split_ctx;      // splits of the context keys (+1 in-chunk split)
   int tiles_per_split;  // 32-key tiles per context split
-  size_t part_bytes;    // partial outputs, after the score workspace
+  size_t part_bytes;    // partial outputs and row (max, sum) partials, after the
+                        // score workspace
+  size_t opart_bytes;   // the partial outputs' share of part_bytes
 };
 AttnPlan attn_plan(kvz_dtype dt, const ScorePlan& p);
+// bf16: the whole fused call (output pass forming the row (max, sum) partials
+// and O, the score update from those partials, the output merge); fp32: the
+// output after a kvz_score_chunk-style score update of the same call
 hipError_t attn_launch(kvz_dtype dt, const ScorePlan& p, const AttnPlan& a, const void* q,
                        const void* kc, const void* kin, const void* vc, const void* vin,
-                       float scale, float* O, void* ws, hipStream_t st);
+                       float scale, float* S, float* O, void* ws, hipStream_t st);
 
 hipError_t head_scores_launch(const float* S, int64_t n_heads, int n_c, float* out,
                               hipStream_t st);

@@ -809,6 +809,25 @@ hipError_t launch_bf16(const ScorePlan& p, const void* q, const void* kc, const 
   return hipGetLastError();
 }
 
+// the score update from per-split row (max, sum) partials formed elsewhere
+// (the fused attention-output pass): split merge into the pass-2 row offsets,
+// then pass 2
+template <int D>
+hipError_t launch_finish_bf16(const ScorePlan& p, const float2* part, int splits, const void* q,
+                              const void* kc, float scale, float* S, void* ws, hipStream_t st) {
+  const float cl2 = scale * 1.4426950408889634f;
+  float* lse2 = reinterpret_cast<float*>(reinterpret_cast<char*>(ws) + p.part_bytes);
+  const int nc = p.H * p.R_pad;
+  KVZ_LAUNCH("score_combine", score_combine, (nc + 255) / 256, 256, 0, st, part, lse2, splits,
+             p.R, p.R_pad, p.H, -1.0f / cl2);
+  const int n_kt = (p.n_c + P2Shape<D>::KEYS - 1) / P2Shape<D>::KEYS;
+  const int nb2 = p.H * n_kt;
+  const P2Args a2{(const uint16_t*)q, (const uint16_t*)kc, lse2, S, p.G, p.n_c, p.n_in, p.R,
+                  p.R_pad, n_kt, cl2, scale, nb2};
+  KVZ_LAUNCH("score_pass2", (score_pass2_bf16<D, 0>), xcd_padded_grid(nb2), 256, 0, st, a2);
+  return hipGetLastError();
+}
+
 template <int D, int MODE>
 hipError_t launch_f32(const ScorePlan& p, const void* q, const void* kc, const void* kin,
                       float scale, float* S, void* ws, hipStream_t st) {
@@ -877,6 +896,16 @@ ScorePlan score_plan(kvz_dtype dt, int H, int G, int n_in, int d, int n_c) {
   p.lse_bytes = align256((size_t)H * p.R_pad * sizeof(float));
   p.total_bytes = p.part_bytes + p.lse_bytes;
   return p;
+}
+
+hipError_t score_finish_launch(const ScorePlan& p, const float2* part, int splits, const void* q,
+                               const void* kc, float scale, float* S, void* ws, hipStream_t st) {
+  switch (p.d) {
+    case 64: return launch_finish_bf16<64>(p, part, splits, q, kc, scale, S, ws, st);
+    case 128: return launch_finish_bf16<128>(p, part, splits, q, kc, scale, S, ws, st);
+    case 256: return launch_finish_bf16<256>(p, part, splits, q, kc, scale, S, ws, st);
+  }
+  return hipErrorInvalidValue;
 }
 
 hipError_t score_launch(kvz_dtype dt, kvz_aggregate agg, const ScorePlan& p, const void* q,

@@ -112,8 +112,10 @@ def test_small_f32_shapes(case):
         assert_scores_close(O[k], Or[k], atol=1e-5, rtol=1e-4, what=f"{name} O chunk {k}")
 
 
-def test_scores_equal_kvz_score_chunk_bitwise():
-    """The fused call's score update is the plain score call's, bit for bit."""
+def test_scores_match_kvz_score_chunk():
+    """The fused call's score update equals the plain score call's up to the
+    rounding of the row log-sum-exp (the output pass forms the row sums over
+    its own key splits): within 1e-5 relative."""
     wl = Workload("same", 22, 1, 2, 4, 128, 1100, 400, 16, 0.3, key_lognormal_sigma=0.5, sink=True)
     gen = HostGen(wl)
     S, _ = run_chunks(gen, 0, [0, 1, 2])
@@ -124,7 +126,7 @@ def test_scores_equal_kvz_score_chunk_bitwise():
         q, kin = gen.chunk_inputs(0, k)
         kvz.kvz_score_chunk(to_dev(q, "bf16"), kc_d, to_dev(kin, "bf16"), S2, wl.n_prompt,
                             1 / math.sqrt(128))
-    assert np.array_equal(S, S2.cpu().numpy())
+    np.testing.assert_allclose(S, S2.cpu().numpy(), rtol=1e-5, atol=1e-12)
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
