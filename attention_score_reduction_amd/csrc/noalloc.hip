@@ -62,7 +62,7 @@ extern "C" kvz_status kvz_score_chunk_noalloc(kvz_dtype dt, int H, int G, int d,
                                               float* S, void* stream) {
   if (dt != KVZ_BF16 && dt != KVZ_F32) return KVZ_ERR_UNSUPPORTED;
   if (d != 64 && d != 128 && d != 256) return KVZ_ERR_UNSUPPORTED;
-  if (H < 1 || G < 1 || n_in < 1 || n_c < 1 || n_prompt < 0 || n_prompt > n_in)
+  if (H < 1 || H > 4096 || G < 1 || n_in < 1 || n_c < 1 || n_prompt < 0 || n_prompt > n_in)
     return KVZ_ERR_INVALID_ARG;
   if ((long long)G * n_in > (1 << 20) || n_c > (1 << 24) ||
       (long long)n_c * d * 2 > 0x7fffffffLL)

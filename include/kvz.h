@@ -50,7 +50,16 @@ extern "C" {
 
 #define KVZ_API __attribute__((visibility("default")))
 
-typedef enum {
+/* The enums are int-sized in C.  In C++ they get a fixed int underlying type,
+ * so that any int a caller passes (an out-of-range value included, which the
+ * calls reject) is a valid value of the enum type: the ABI is the same. */
+#ifdef __cplusplus
+#define KVZ_ENUM enum : int
+#else
+#define KVZ_ENUM enum
+#endif
+
+typedef KVZ_ENUM {
   KVZ_OK = 0,
   KVZ_ERR_INVALID_ARG = 1,     /* null pointer, bad size, misalignment      */
   KVZ_ERR_UNSUPPORTED = 2,     /* head_dim not in {64,128,256}, bad dtype   */
@@ -58,13 +67,13 @@ typedef enum {
   KVZ_ERR_HIP = 4              /* a HIP launch or runtime call failed       */
 } kvz_status;
 
-typedef enum {
+typedef KVZ_ENUM {
   KVZ_BF16 = 0,                /* bfloat16 inputs, fp32 accumulation        */
   KVZ_F32 = 1                  /* fp32 inputs, fp32 arithmetic              */
 } kvz_dtype;
 
 /* How a context key's per-row attention is aggregated into its score. */
-typedef enum {
+typedef KVZ_ENUM {
   KVZ_AGG_MAX = 0,     /* max over g, i of the softmax probability (the method,
                           blog 4.3.2); S starts at 0                          */
   KVZ_AGG_SUM = 1,     /* sum over g, i (and chunks) of the probability: the
@@ -107,7 +116,7 @@ KVZ_API const char* kvz_build_id(void);
  *
  * Limits: d in {64, 128, 256}; 1 <= n_in, 1 <= n_c <= 2^24 with one head's
  * keys under 2 GiB (n_c * d * 2 <= 2^31 - 1, i.e. n_c <= 4,194,303 at d=256
- * and 8,388,607 at d=128), 1 <= H, 1 <= G,
+ * and 8,388,607 at d=128), 1 <= H <= 4096, 1 <= G,
  * G * n_in <= 2^20.  Workspace: kvz_score_chunk_workspace() bytes, 256-byte
  * aligned, device memory.
  * ---------------------------------------------------------------------- */

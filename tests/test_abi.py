@@ -82,6 +82,7 @@ def _score(**kw):
     # one head's keys past 2 GiB (the 32-bit range of the buffer loads)
     (dict(d=256, n_c=4194304), kvz.KVZ_ERR_INVALID_ARG),
     (dict(d=128, n_c=8388608), kvz.KVZ_ERR_INVALID_ARG),
+    (dict(H=4097), kvz.KVZ_ERR_INVALID_ARG),          # more KV heads than one call takes
 ])
 def test_score_validation(kw, status):
     assert _score(**kw) == status
@@ -117,6 +118,9 @@ def test_score_attn_workspace_covers_score_workspace():
     assert kvz.kvz_score_chunk_attn_workspace(kvz.KVZ_BF16, 8, 4, 2064, 256, 4194304) == 0
     assert kvz.kvz_score_chunk_workspace(kvz.KVZ_BF16, 8, 4, 2064, 256, 4194304) == 0
     assert kvz.kvz_score_chunk_workspace(kvz.KVZ_BF16, 8, 4, 2064, 256, 4194303) > 0
+    assert kvz.kvz_score_chunk_workspace(kvz.KVZ_BF16, 4096, 4, 2064, 128, 8192) > 0
+    assert kvz.kvz_score_chunk_workspace(kvz.KVZ_BF16, 4097, 4, 2064, 128, 8192) == 0
+    assert kvz.kvz_score_chunk_attn_workspace(kvz.KVZ_BF16, 4097, 4, 2064, 128, 8192) == 0
     # exactly the required size passes validation, one byte less does not
     need = kvz.kvz_score_chunk_attn_workspace(kvz.KVZ_BF16, 2, 4, 20, 128, 100)
     assert _attn(wsb=need - 1) == kvz.KVZ_ERR_WORKSPACE
