@@ -4,6 +4,8 @@
 #include <math.h>
 #include <string.h>
 
+#include <atomic>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -19,35 +21,46 @@ struct ProfRec {
   std::string name;
   hipEvent_t a, b;
 };
+// All fields but `on` are guarded by mu; `on` lets a launch skip the lock
+// while the timer is off.  Each thread keeps the index of its own open record
+// (t_pending), so launches from several threads pair their events correctly.
 struct Prof {
-  bool on = false;
+  std::atomic<bool> on{false};
+  std::mutex mu;
   int max_launches = 0;
+  uint64_t epoch = 0;  // bumped by every enable/disable: stale pending indexes are dropped
   std::vector<hipEvent_t> pool;
   std::vector<ProfRec> recs;
-  int pending = -1;
 };
 Prof& prof() {
   static Prof p;
   return p;
 }
+thread_local int t_pending = -1;
+thread_local uint64_t t_epoch = 0;
 }  // namespace
 
 void prof_before(const char* name, hipStream_t s) {
+  t_pending = -1;
   Prof& p = prof();
-  p.pending = -1;
-  if (!p.on || (int)p.recs.size() >= p.max_launches) return;
+  if (!p.on.load(std::memory_order_acquire)) return;
+  std::lock_guard<std::mutex> g(p.mu);
+  if (!p.on.load(std::memory_order_relaxed) || (int)p.recs.size() >= p.max_launches) return;
   const size_t k = p.recs.size();
   ProfRec r{name, p.pool[2 * k], p.pool[2 * k + 1]};
   if (hipEventRecord(r.a, s) != hipSuccess) return;
   p.recs.push_back(r);
-  p.pending = (int)k;
+  t_pending = (int)k;
+  t_epoch = p.epoch;
 }
 
 void prof_after(hipStream_t s) {
+  if (t_pending < 0) return;
   Prof& p = prof();
-  if (p.pending < 0) return;
-  (void)hipEventRecord(p.recs[p.pending].b, s);
-  p.pending = -1;
+  std::lock_guard<std::mutex> g(p.mu);
+  if (t_epoch == p.epoch && t_pending < (int)p.recs.size())
+    (void)hipEventRecord(p.recs[t_pending].b, s);
+  t_pending = -1;
 }
 
 }  // namespace kvz
@@ -326,26 +339,28 @@ kvz_status kvz_decode_packed(kvz_dtype dt, int64_t n_heads, int G, int d, int ma
 }
 
 kvz_status kvz_prof_enable(int on, int max_launches) {
+  if (on && max_launches < 1) return KVZ_ERR_INVALID_ARG;
   Prof& p = prof();
+  std::lock_guard<std::mutex> g(p.mu);
+  p.on.store(false, std::memory_order_release);
+  ++p.epoch;
   for (hipEvent_t e : p.pool) (void)hipEventDestroy(e);
   p.pool.clear();
   p.recs.clear();
-  p.on = false;
-  p.pending = -1;
   if (!on) return KVZ_OK;
-  if (max_launches < 1) return KVZ_ERR_INVALID_ARG;
   p.pool.resize(2 * (size_t)max_launches);
   for (auto& e : p.pool)
     if (hipEventCreate(&e) != hipSuccess) return KVZ_ERR_HIP;
   p.max_launches = max_launches;
   p.recs.reserve(max_launches);
-  p.on = true;
+  p.on.store(true, std::memory_order_release);
   return KVZ_OK;
 }
 
 kvz_status kvz_prof_read(const char* name, int64_t* launches, double* total_ms) {
   if (!name || !launches || !total_ms) return KVZ_ERR_INVALID_ARG;
   Prof& p = prof();
+  std::lock_guard<std::mutex> g(p.mu);
   int64_t n = 0;
   double ms = 0.0;
   bool known = false;
@@ -354,7 +369,7 @@ kvz_status kvz_prof_read(const char* name, int64_t* launches, double* total_ms) 
                                  "select_pick",     "select_fixup",   "select_scan",
                                  "select_mask",     "compact_count",  "compact_scan",
                                  "compact_scatter", "head_scores",    "token_scores",
-                                 "decode_split",    "decode_combine", "attn_pass3",
+                                 "decode_split",    "decode_combine", "attn_flash",
                                  "attn_reduce",     "evict_mask",     "evict_offsets"};
   for (const char* k : kNames) known |= strcmp(k, name) == 0;
   if (!known) return KVZ_ERR_INVALID_ARG;

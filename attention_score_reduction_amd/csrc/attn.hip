@@ -412,7 +412,7 @@ hipError_t launch3(kvz_dtype dt, const ScorePlan& p, const AttnPlan& a, const vo
                                                a.opart_bytes);
     const int splits = a.n_split_ctx + 1;
     const int nb = p.H * splits * a.n_rt;
-    KVZ_LAUNCH("attn_pass3", attn_flash_bf16<D>, xcd_padded_grid(nb), 256, 0, st,
+    KVZ_LAUNCH("attn_flash", attn_flash_bf16<D>, xcd_padded_grid(nb), 256, 0, st,
                (const uint16_t*)q, (const uint16_t*)kc, (const uint16_t*)kin,
                (const uint16_t*)vc, (const uint16_t*)vin, opart, mlpart, p.H, p.G, p.n_c, p.n_in,
                p.R, p.R_pad, a.n_rt, a.n_split_ctx, a.tiles_per_split, cl2, nb);
@@ -426,7 +426,7 @@ hipError_t launch3(kvz_dtype dt, const ScorePlan& p, const AttnPlan& a, const vo
   } else {
     const float* lse2 = reinterpret_cast<const float*>(ws);
     dim3 grid(p.R, p.H);
-    KVZ_LAUNCH("attn_pass3", attn_f32<D>, grid, 64, 0, st, (const float*)q, (const float*)kc,
+    KVZ_LAUNCH("attn_flash", attn_f32<D>, grid, 64, 0, st, (const float*)q, (const float*)kc,
                (const float*)kin, (const float*)vc, (const float*)vin, lse2, O, p.G, p.n_c,
                p.n_in, p.R_pad, cl2);
   }

@@ -385,7 +385,7 @@ def attn_output(kvz, wl, data, scale, stream):
     call()
     torch.cuda.synchronize()
     reps = 5
-    pr = prof_window(kvz, SCORE_KERNELS + ("attn_pass3", "attn_reduce"),
+    pr = prof_window(kvz, SCORE_KERNELS + ("attn_flash", "attn_reduce"),
                      lambda: [call() for _ in range(reps)], 16 * reps)
     at = {nm: round(ms / n * 1e3, 2) for nm, (n, ms) in pr.items()}
     vis = H * G * (n_in0 * n_c + n_in0 * (n_in0 + 1) // 2)
@@ -393,10 +393,10 @@ def attn_output(kvz, wl, data, scale, stream):
     out = {"per_call_us": at, "call_us": round(sum(at.values()), 2),
            "what": "kvz_score_chunk_attn on one 16+2048-row chunk of one layer (all KV heads): "
                    "scores plus O = P[V_c; V_in]"}
-    if "attn_pass3" in at:
-        ach = o_flops / (at["attn_pass3"] * 1e-6) / 1e12
-        out.update({"pass3_flops": o_flops, "pass3_TFLOPs": round(ach, 2),
-                    "pass3_frac": round(ach / MFMA_BF16_PEAK_TFLOPS, 4)})
+    if "attn_flash" in at:
+        ach = o_flops / (at["attn_flash"] * 1e-6) / 1e12
+        out.update({"flash_flops": o_flops, "flash_TFLOPs": round(ach, 2),
+                    "flash_frac": round(ach / MFMA_BF16_PEAK_TFLOPS, 4)})
     return out
 
 

@@ -319,14 +319,15 @@ KVZ_API kvz_status kvz_decode_packed(kvz_dtype dt, int64_t n_heads, int G, int d
 
 /* ------------------------------------------------------------------------
  * Optional kernel timer (measurement only).
- * The timer is process-global state and is not thread-safe: enable, read and
- * disable it from one thread, with no launching call running on another
- * thread meanwhile.  Disabled (the default), it costs one branch per launch
- * and every other call is reentrant.
+ * The timer is the library's one piece of process-wide state; it is guarded
+ * by a lock and safe to use from several threads.  Disabled (the default), it
+ * costs one atomic load per launch; enabled, one lock per launch.  A call
+ * that launches while another thread enables or disables the timer may leave
+ * its launch untimed.
  * While enabled, every kernel the library launches is bracketed by a pair of
  * HIP events on its stream.  kvz_prof_read() synchronises those events and
  * returns, for the kernel named `name` ("score_pass1", "score_combine",
- * "score_pass2", "attn_pass3", "attn_reduce", "select_*", "compact_*",
+ * "score_pass2", "attn_flash", "attn_reduce", "select_*", "compact_*",
  * "head_scores", "token_scores", "evict_mask", "evict_offsets",
  * "decode_split", "decode_combine"), the
  * number of launches and the
