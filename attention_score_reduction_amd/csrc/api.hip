@@ -301,6 +301,9 @@ kvz_status kvz_compact(kvz_dtype dt, int d, int n_c, int64_t head_begin, int64_t
       (reinterpret_cast<uintptr_t>(ws) & 255u) != 0)
     return KVZ_ERR_INVALID_ARG;
   const CompactPlan p = compact_plan(head_count, n_c);
+  // one 256-thread scatter workgroup per 64 positions: the launch's
+  // work-item count must fit in 32 bits
+  if (p.n_tiles >= (int64_t(1) << 24)) return KVZ_ERR_INVALID_ARG;
   if (ws_bytes < p.total_bytes) return KVZ_ERR_WORKSPACE;
   const int row_bytes = d * (dt == KVZ_BF16 ? 2 : 4);
   clear_error();
@@ -367,7 +370,7 @@ kvz_status kvz_prof_read(const char* name, int64_t* launches, double* total_ms) 
   static const char* kNames[] = {"score_pass1",     "score_combine",  "score_pass2",
                                  "select_empty",    "select_init",    "select_hist",
                                  "select_pick",     "select_fixup",   "select_scan",
-                                 "select_mask",     "compact_count",  "compact_scan",
+                                 "select_mask",     "compact_offsets",
                                  "compact_scatter", "head_scores",    "token_scores",
                                  "decode_split",    "decode_combine", "attn_flash",
                                  "attn_reduce",     "evict_mask",     "evict_offsets"};

@@ -328,7 +328,7 @@ def structured_evictions(kvz, wl, S, kc_flat, vc_flat, n_sink=64, n_recent=1024)
     idx = torch.empty(cap, dtype=torch.int32, device=dev)
     names = ("head_scores", "token_scores", "select_init", "select_hist", "select_pick",
              "select_fixup", "select_scan", "select_mask", "select_empty", "evict_mask",
-             "evict_offsets", "compact_count", "compact_scan", "compact_scatter")
+             "evict_offsets", "compact_offsets", "compact_scatter")
     out = {}
     for mode in ("heads", "tokens"):
         rows = rows_h if mode == "heads" else rows_t
@@ -589,8 +589,8 @@ def main():
     ms_per_step = (t1 - t0) * 1000.0 / args.steps
 
     names = ["score_pass1", "score_combine", "score_pass2", "select_init", "select_hist",
-             "select_pick", "select_fixup", "select_scan", "select_mask", "compact_count",
-             "compact_scan", "compact_scatter"]
+             "select_pick", "select_fixup", "select_scan", "select_mask", "compact_offsets",
+             "compact_scatter"]
     kern = {}
     for nm in names:
         n, ms = kvz.kvz_prof_read(nm)

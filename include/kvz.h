@@ -283,7 +283,9 @@ KVZ_API kvz_status kvz_select_threshold(const float* S, int64_t n_heads, int n_c
  *                 for absolute head h, the r-th kept j (ascending) goes to
  *                 row head_offsets[h] + r, with idx_out = j.
  * Rows are copied bit-exactly.  Workspace: kvz_compact_workspace() bytes.
- * Limits: d in {64, 128, 256}.
+ * Limits: d in {64, 128, 256}; (head_begin + head_count) * n_c < 2^31;
+ * head_count * ceil(n_c / 64) < 2^24 (about 2^30 positions per call).
+ * KVZ_ERR_INVALID_ARG otherwise, before anything is launched.
  * ---------------------------------------------------------------------- */
 KVZ_API size_t kvz_compact_workspace(int64_t head_count, int n_c);
 

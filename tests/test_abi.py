@@ -186,6 +186,10 @@ def test_compact_validation():
     assert f(vc=MIS) == kvz.KVZ_ERR_INVALID_ARG
     assert f(idx=P(4098)) == kvz.KVZ_ERR_INVALID_ARG
     assert f(wsb=8) == kvz.KVZ_ERR_WORKSPACE
+    # positions beyond the int32 range, then a launch of 2^24 scatter
+    # workgroups (2^32 work-items) while the positions still fit
+    assert f(nc=1 << 22, hc=1 << 9) == kvz.KVZ_ERR_INVALID_ARG
+    assert f(nc=1 << 21, hc=1 << 9) == kvz.KVZ_ERR_INVALID_ARG
 
 
 def test_prof_read_rejects_unknown_name():

@@ -93,7 +93,7 @@ def test_select_full_size_scores():
     check_select(S, K)
 
 
-def _compact_case(wl, dtype, K_ratio, per_layer):
+def _compact_case(wl, dtype, K_ratio, per_layer, mask_offset=0):
     rng = np.random.default_rng(wl.seed)
     n_heads, n_c, d = wl.n_heads, wl.n_ctx, wl.head_dim
     if dtype == "bf16":
@@ -107,6 +107,12 @@ def _compact_case(wl, dtype, K_ratio, per_layer):
     K = kvz.kvz_keep_count(S.size, K_ratio)
     Sd = torch.from_numpy(S).cuda()
     mask, offs, _ = kvz.kvz_select_threshold(Sd, K)
+    if mask_offset:
+        # the same mask at an address that is not 16-byte aligned: the
+        # compaction counts it with byte loads instead of 16-byte loads
+        buf = torch.zeros(mask.numel() + mask_offset, dtype=torch.uint8, device="cuda")
+        buf[mask_offset:].copy_(mask)
+        mask = buf[mask_offset:]
     kc_d, vc_d = to_dev(kc, dtype), to_dev(vc, dtype)
     tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
     ko = torch.empty(K, d, dtype=tdt, device="cuda")
@@ -132,9 +138,18 @@ def _compact_case(wl, dtype, K_ratio, per_layer):
 
 @pytest.mark.parametrize("per_layer", [False, True])
 @pytest.mark.parametrize("d", [64, 128, 256])
-def test_compact_bit_exact(d, per_layer):
-    wl = Workload("cmp", 20 + d, 3, 2, 1, d, 9000, 2048, 16, 0.3)
+@pytest.mark.parametrize("n_c", [9000, 9008])
+def test_compact_bit_exact(d, per_layer, n_c):
+    # n_c = 9008, a multiple of 16: mask rows counted with 16-byte loads;
+    # 9000: byte loads and a ragged last tile in every head
+    wl = Workload("cmp", 20 + d, 3, 2, 1, d, n_c, 2048, 16, 0.3)
     _compact_case(wl, "bf16", 0.3, per_layer)
+
+
+@pytest.mark.parametrize("per_layer", [False, True])
+def test_compact_unaligned_mask(per_layer):
+    wl = Workload("cmpu", 27, 2, 3, 1, 128, 4112, 2048, 16, 0.3)
+    _compact_case(wl, "bf16", 0.3, per_layer, mask_offset=1)
 
 
 def test_compact_f32_and_extremes():
