@@ -37,18 +37,29 @@ def _case(n_heads, G, d, lens, dtype, seed):
 @pytest.mark.parametrize("d", [64, 128, 256])
 @pytest.mark.parametrize("G", [1, 2, 4, 5, 8])
 def test_decode_variable_lengths(d, G):
-    lens = [0, 1, 3, 17, 64, 1023, 1024, 1025, 5000]
+    # around one segment of rows (2048) and past it
+    lens = [0, 1, 3, 17, 64, 1023, 1024, 1025, 2047, 2048, 2049, 5000]
     got, ref = _case(len(lens), G, d, lens, "bf16", d * 10 + G)
     assert_scores_close(got, ref, atol=1e-4, rtol=1e-3, what=f"decode d={d} G={G}")
 
 
 @pytest.mark.parametrize("d,G", [(128, 4), (64, 2), (256, 1)])
 def test_decode_long_heads(d, G):
-    """Heads of up to 20 segments of 1024 rows: the segment merge takes
+    """Heads of up to 20 segments of 2048 rows: the segment merge takes
     several batches of eight, including a partial last batch."""
-    lens = [8191, 8192, 8193, 20000, 3, 16385]
+    lens = [8191, 8192, 8193, 20000, 3, 16385, 40000]
     got, ref = _case(len(lens), G, d, lens, "bf16", 7 * d + G)
     assert_scores_close(got, ref, atol=1e-4, rtol=1e-3, what=f"decode long d={d} G={G}")
+
+
+def test_decode_longest_segments():
+    """64 heads with a longest head of 131072 rows (64 segments of 2048
+    rows); the other heads are short and most of their segments are empty."""
+    rng = np.random.default_rng(99)
+    lens = [int(x) for x in rng.integers(0, 3000, 64)]
+    lens[17] = 131072
+    got, ref = _case(len(lens), 2, 64, lens, "bf16", 98)
+    assert_scores_close(got, ref, atol=1e-4, rtol=1e-3, what="decode 2048-row segments")
 
 
 def test_decode_fp32_and_dense_baseline():
