@@ -112,6 +112,34 @@ def test_small_f32_shapes(case):
         assert_scores_close(O[k], Or[k], atol=1e-5, rtol=1e-4, what=f"{name} O chunk {k}")
 
 
+DEGENERATE = [
+    # (name, H, G, d, n_c, chunk, n_prompt, dtype): one context key and one
+    # query row, contexts shorter than one 32-key tile, no prompt rows, wide
+    # query groups
+    ("one_key_one_row", 1, 1, 128, 1, 1, 0, "bf16"),
+    ("ctx5_no_prompt", 2, 2, 64, 5, 3, 0, "bf16"),
+    ("ctx31_g8", 1, 8, 128, 31, 33, 4, "bf16"),
+    ("g16_d256", 1, 16, 256, 200, 70, 5, "bf16"),
+    ("f32_one_key_one_row", 1, 1, 64, 1, 1, 0, "f32"),
+    ("f32_g16", 2, 16, 64, 90, 40, 3, "f32"),
+]
+
+
+@pytest.mark.parametrize("case", DEGENERATE, ids=[c[0] for c in DEGENERATE])
+def test_degenerate_shapes(case):
+    name, H, G, d, n_c, chunk, n_p, dtype = case
+    wl = Workload(name, 26, 1, H, G, d, n_c, chunk, n_p, 0.3, dtype=dtype)
+    gen = HostGen(wl)
+    ids = list(range(len(wl.chunks())))
+    S, O = run_chunks(gen, 0, ids)
+    Sr, Or = oracle_chunks(gen, 0, ids, list(range(H)))
+    s_tol = dict(atol=1e-6, rtol=1e-4) if dtype == "f32" else {}
+    o_tol = dict(atol=1e-5, rtol=1e-4) if dtype == "f32" else dict(atol=O_ATOL, rtol=O_RTOL)
+    assert_scores_close(S, Sr, what=f"{name} S", **s_tol)
+    for k in ids:
+        assert_scores_close(O[k], Or[k], what=f"{name} O chunk {k}", **o_tol)
+
+
 def test_scores_match_kvz_score_chunk():
     """The fused call's score update equals the plain score call's up to the
     rounding of the row log-sum-exp (the output pass forms the row sums over

@@ -158,6 +158,33 @@ def test_small_f32_shapes(case):
     assert_scores_close(got, ref, atol=1e-6, rtol=1e-4, what=name)
 
 
+DEGENERATE = [
+    # (name, H, G, d, n_c, chunk, n_prompt, dtype): shapes at the edges of
+    # the tiling: one context key and one query row, contexts shorter than
+    # one 32-key tile, no prompt rows, wide query groups (rows i-major, so a
+    # 32-row tile spans few tokens)
+    ("one_key_one_row", 1, 1, 128, 1, 1, 0, "bf16"),
+    ("ctx5_no_prompt", 2, 2, 64, 5, 3, 0, "bf16"),
+    ("ctx31_g8", 1, 8, 128, 31, 33, 4, "bf16"),
+    ("g16_d256", 1, 16, 256, 200, 70, 5, "bf16"),
+    ("f32_one_key_one_row", 1, 1, 64, 1, 1, 0, "f32"),
+    ("f32_g16", 2, 16, 64, 90, 40, 3, "f32"),
+]
+
+
+@pytest.mark.parametrize("case", DEGENERATE, ids=[c[0] for c in DEGENERATE])
+def test_degenerate_shapes(case):
+    name, H, G, d, n_c, chunk, n_p, dtype = case
+    wl = Workload(name, 16, 1, H, G, d, n_c, chunk, n_p, 0.3, dtype=dtype)
+    gen = HostGen(wl)
+    ref = oracle_layer_scores(gen, 0, list(range(H)))
+    got = gpu_layer_scores(gen, 0)
+    if dtype == "f32":
+        assert_scores_close(got, ref, atol=1e-6, rtol=1e-4, what=name)
+    else:
+        assert_scores_close(got, ref, what=name)
+
+
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 def test_resume_from_saved_scores_is_bitwise_identical(dtype):
     """Scoring can stop after any chunk and resume from a host copy of S: the
