@@ -62,6 +62,29 @@ struct Row8<float> {
   }
 };
 
+// v moved across lanes by a DPP pattern (a modifier of the VALU instruction
+// that consumes it: no LDS traffic, unlike a general lane shuffle)
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, true));
+}
+
+// Sum of s over each aligned group of LPR lanes, in every lane of the group:
+// pairs (quad_perm 1,0,3,2), quads (quad_perm 2,3,0,1), then the mirror
+// images of the half row (lane i of 8 <- 7 - i) and of the row (lane i of 16
+// <- 15 - i), each of which lands on the other, already summed, half; past
+// 16 lanes one shuffle.
+template <int LPR>
+__device__ __forceinline__ float group_sum(float s) {
+  s += dpp_f<0xB1>(s);
+  s += dpp_f<0x4E>(s);
+  if constexpr (LPR >= 8) s += dpp_f<0x141>(s);
+  if constexpr (LPR >= 16) s += dpp_f<0x140>(s);
+  if constexpr (LPR >= 32) s += __shfl_xor(s, 16);
+  static_assert(LPR >= 4 && LPR <= 32, "lanes per row");
+  return s;
+}
+
 // partial state per (head, segment, g): m (log2 domain), l, acc[D]
 template <int D>
 __device__ __forceinline__ size_t part_off(int64_t h, int seg, int n_seg, int g, int G) {
@@ -124,8 +147,7 @@ __global__ __launch_bounds__(TPB) void decode_split(const T* __restrict__ q,
         float s = 0.f;
 #pragma unroll
         for (int i = 0; i < 8; ++i) s = fmaf(qv[g][i], kf[j][i], s);
-#pragma unroll
-        for (int off = 1; off < LPR; off <<= 1) s += __shfl_xor(s, off);
+        s = group_sum<LPR>(s);
         x[j] = ok[j] ? s * cl2 : -INFINITY;
       }
       float mn = m[g];
