@@ -28,31 +28,107 @@ namespace {
 
 constexpr int TPB = 256;
 
-// one workgroup per head: max over n_c scores
-__global__ __launch_bounds__(TPB) void head_max(const float* __restrict__ S, int n_c,
-                                                float* __restrict__ out) {
-  __shared__ float red[TPB / 64];
+constexpr int HM_TPB = 1024;  // head_max: one workgroup of 16 waves per head
+
+__device__ __forceinline__ float max4(float4 v) { return fmaxf(fmaxf(v.x, v.y), fmaxf(v.z, v.w)); }
+
+// One workgroup per head: max over its n_c scores.  With n_c a multiple of 4
+// every row is 16-byte aligned (S is), so each thread takes 16-byte loads,
+// four in flight; otherwise 4-byte loads.  (One 256-thread workgroup with
+// 4-byte loads read the 128K cache's scores at 2.8 TB/s.)
+__global__ __launch_bounds__(HM_TPB) void head_max(const float* __restrict__ S, int n_c,
+                                                   float* __restrict__ out) {
+  __shared__ float red[HM_TPB / 64];
   const int64_t h = blockIdx.x;
   const float* row = S + h * (int64_t)n_c;
+  const int t = threadIdx.x;
   float m = -INFINITY;
-  int j = threadIdx.x;
-  for (; j + 3 * TPB < n_c; j += 4 * TPB)
-    m = fmaxf(fmaxf(m, fmaxf(row[j], row[j + TPB])), fmaxf(row[j + 2 * TPB], row[j + 3 * TPB]));
-  for (; j < n_c; j += TPB) m = fmaxf(m, row[j]);
+  if ((n_c & 3) == 0) {
+    const float4* r4 = reinterpret_cast<const float4*>(row);
+    const int n4 = n_c >> 2;
+    int i = t;
+    for (; i + 3 * HM_TPB < n4; i += 4 * HM_TPB) {
+      const float4 a = r4[i], b = r4[i + HM_TPB], c = r4[i + 2 * HM_TPB], d = r4[i + 3 * HM_TPB];
+      m = fmaxf(m, fmaxf(fmaxf(max4(a), max4(b)), fmaxf(max4(c), max4(d))));
+    }
+    for (; i < n4; i += HM_TPB) m = fmaxf(m, max4(r4[i]));
+  } else {
+    int j = t;
+    for (; j + 3 * HM_TPB < n_c; j += 4 * HM_TPB)
+      m = fmaxf(fmaxf(m, fmaxf(row[j], row[j + HM_TPB])),
+                fmaxf(row[j + 2 * HM_TPB], row[j + 3 * HM_TPB]));
+    for (; j < n_c; j += HM_TPB) m = fmaxf(m, row[j]);
+  }
   for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
-  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
+  if ((t & 63) == 0) red[t >> 6] = m;
   __syncthreads();
-  if (threadIdx.x == 0) out[h] = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  if (t < 64) {
+    float v = t < HM_TPB / 64 ? red[t] : -INFINITY;
+    for (int off = 32; off > 0; off >>= 1) v = fmaxf(v, __shfl_xor(v, off));
+    if (t == 0) out[h] = v;
+  }
 }
 
-// one thread per token: max over all heads (coalesced across threads)
+// Token maxima over all heads.  A workgroup covers 256 consecutive tokens,
+// four per lane (one 16-byte load per head when n_c is a multiple of 4, so
+// that rows stay 16-byte aligned); its four waves take every fourth head,
+// eight loads in flight, and LDS merges the waves.  (One thread per token
+// over all heads read the 128K cache's scores at 1.9 TB/s.)
+constexpr int TM_U = 8;
 __global__ __launch_bounds__(TPB) void token_max(const float* __restrict__ S, int64_t n_heads,
                                                  int n_c, float* __restrict__ out) {
-  const int j = blockIdx.x * TPB + threadIdx.x;
-  if (j >= n_c) return;
-  float m = -INFINITY;
-  for (int64_t h = 0; h < n_heads; ++h) m = fmaxf(m, S[h * (int64_t)n_c + j]);
-  out[j] = m;
+  __shared__ float4 red[TPB / 64][64];
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int j0 = blockIdx.x * 256 + lane * 4;
+  float4 m = make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY);
+  if ((n_c & 3) == 0 && j0 < n_c) {  // j0 + 3 < n_c as well
+    const float* col = S + j0;
+    int64_t h = w;
+    for (; h + 4 * (TM_U - 1) < n_heads; h += 4 * TM_U) {
+      float4 v[TM_U];
+#pragma unroll
+      for (int u = 0; u < TM_U; ++u)
+        v[u] = *reinterpret_cast<const float4*>(col + (h + 4 * u) * (int64_t)n_c);
+#pragma unroll
+      for (int u = 0; u < TM_U; ++u) {
+        m.x = fmaxf(m.x, v[u].x);
+        m.y = fmaxf(m.y, v[u].y);
+        m.z = fmaxf(m.z, v[u].z);
+        m.w = fmaxf(m.w, v[u].w);
+      }
+    }
+    for (; h < n_heads; h += 4) {
+      const float4 v = *reinterpret_cast<const float4*>(col + h * (int64_t)n_c);
+      m.x = fmaxf(m.x, v.x);
+      m.y = fmaxf(m.y, v.y);
+      m.z = fmaxf(m.z, v.z);
+      m.w = fmaxf(m.w, v.w);
+    }
+  } else if (j0 < n_c) {
+    float r[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+    for (int64_t h = w; h < n_heads; h += 4)
+#pragma unroll
+      for (int c = 0; c < 4; ++c)
+        if (j0 + c < n_c) r[c] = fmaxf(r[c], S[h * (int64_t)n_c + j0 + c]);
+    m = make_float4(r[0], r[1], r[2], r[3]);
+  }
+  red[w][lane] = m;
+  __syncthreads();
+  if (w == 0 && j0 < n_c) {
+    float4 v = red[0][lane];
+#pragma unroll
+    for (int ww = 1; ww < TPB / 64; ++ww) {
+      const float4 o = red[ww][lane];
+      v.x = fmaxf(v.x, o.x);
+      v.y = fmaxf(v.y, o.y);
+      v.z = fmaxf(v.z, o.z);
+      v.w = fmaxf(v.w, o.w);
+    }
+    const float vv[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+      if (j0 + c < n_c) out[j0 + c] = vv[c];
+  }
 }
 
 // bytes f0 .. f0+15 of a flat mask of N bytes, packed little-endian in w:
@@ -203,7 +279,7 @@ hipError_t select_heads_launch(const float* S, int64_t n_heads, int n_c, int64_t
                                int n_sink, int n_recent, uint8_t* mask, int64_t* head_offsets,
                                uint8_t* head_keep, void* ws, hipStream_t st) {
   const AggWs a = carve_agg(n_heads, ws);
-  KVZ_LAUNCH("head_scores", head_max, (unsigned)n_heads, TPB, 0, st, S, n_c, a.agg);
+  KVZ_LAUNCH("head_scores", head_max, (unsigned)n_heads, HM_TPB, 0, st, S, n_c, a.agg);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   e = select_launch(select_plan(1, (int)n_heads), a.agg, K_heads, head_keep, a.sel_offs,
@@ -223,7 +299,7 @@ hipError_t select_tokens_launch(const float* S, int64_t n_heads, int n_c, int64_
                                 uint8_t* mask, int64_t* head_offsets, uint8_t* token_keep,
                                 void* ws, hipStream_t st) {
   const AggWs a = carve_agg(n_c, ws);
-  KVZ_LAUNCH("token_scores", token_max, (unsigned)((n_c + TPB - 1) / TPB), TPB, 0, st, S,
+  KVZ_LAUNCH("token_scores", token_max, (unsigned)((n_c + 255) / 256), TPB, 0, st, S,
              n_heads, n_c, a.agg);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
@@ -242,13 +318,13 @@ hipError_t select_tokens_launch(const float* S, int64_t n_heads, int n_c, int64_
 
 hipError_t head_scores_launch(const float* S, int64_t n_heads, int n_c, float* out,
                               hipStream_t st) {
-  KVZ_LAUNCH("head_scores", head_max, (unsigned)n_heads, TPB, 0, st, S, n_c, out);
+  KVZ_LAUNCH("head_scores", head_max, (unsigned)n_heads, HM_TPB, 0, st, S, n_c, out);
   return hipGetLastError();
 }
 
 hipError_t token_scores_launch(const float* S, int64_t n_heads, int n_c, float* out,
                                hipStream_t st) {
-  KVZ_LAUNCH("token_scores", token_max, (unsigned)((n_c + TPB - 1) / TPB), TPB, 0, st, S, n_heads,
+  KVZ_LAUNCH("token_scores", token_max, (unsigned)((n_c + 255) / 256), TPB, 0, st, S, n_heads,
              n_c, out);
   return hipGetLastError();
 }
