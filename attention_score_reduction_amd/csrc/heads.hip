@@ -231,6 +231,41 @@ __global__ __launch_bounds__(TPB) void token_broadcast_mask(const uint8_t* __res
   }
 }
 
+// The two mask writers when n_c is a multiple of 16 (and the keep array is
+// 16-byte aligned): a 16-byte group g then lies in one head row, at offset
+// 16 * (g % groups per row), and 32-bit index arithmetic suffices (N < 2^31).
+// Token eviction: the group is the keep row's 16 bytes at that offset.
+__global__ __launch_bounds__(TPB) void token_broadcast_mask16(const uint4* __restrict__ tkeep,
+                                                              int gpr, int groups,
+                                                              uint4* __restrict__ mask) {
+  for (int g = blockIdx.x * TPB + threadIdx.x; g < groups; g += gridDim.x * TPB)
+    mask[g] = tkeep[g % gpr];
+}
+
+// Head eviction: all ones when the group's head is kept whole, else byte u is
+// 1 when position 16 * (g % gpr) + u lies in either window.
+__global__ __launch_bounds__(TPB) void head_window_mask16(const uint8_t* __restrict__ keep,
+                                                          int gpr, int groups, int n_c,
+                                                          int n_sink, int n_recent,
+                                                          uint4* __restrict__ mask) {
+  for (int g = blockIdx.x * TPB + threadIdx.x; g < groups; g += gridDim.x * TPB) {
+    const int h = g / gpr;
+    const int j0 = (g - h * gpr) * 16;
+    uint32_t w[4];
+    if (keep[h]) {
+      w[0] = w[1] = w[2] = w[3] = 0x01010101u;
+    } else {
+      w[0] = w[1] = w[2] = w[3] = 0u;
+#pragma unroll
+      for (int u = 0; u < 16; ++u) {
+        const int j = j0 + u;
+        w[u >> 2] |= (uint32_t)(j < n_sink || j >= n_c - n_recent) << (8 * (u & 3));
+      }
+    }
+    mask[g] = make_uint4(w[0], w[1], w[2], w[3]);
+  }
+}
+
 // head offsets of token eviction: every head keeps exactly K tokens
 __global__ void token_offsets(int64_t n_heads, int64_t K, int64_t* __restrict__ offs) {
   const int64_t stride = (int64_t)gridDim.x * blockDim.x;
@@ -288,8 +323,12 @@ hipError_t select_heads_launch(const float* S, int64_t n_heads, int n_c, int64_t
   const int64_t s = n_sink < n_c ? n_sink : n_c, r = n_recent < n_c ? n_recent : n_c;
   const int64_t window = s + r < n_c ? s + r : n_c;
   const int64_t N = n_heads * (int64_t)n_c;
-  KVZ_LAUNCH("evict_mask", head_window_mask, mask_grid(N), TPB, 0, st, head_keep, n_heads, n_c,
-             n_sink, n_recent, mask);
+  if (n_c % 16 == 0)
+    KVZ_LAUNCH("evict_mask", head_window_mask16, mask_grid(N), TPB, 0, st, head_keep,
+               n_c / 16, (int)(N / 16), n_c, n_sink, n_recent, reinterpret_cast<uint4*>(mask));
+  else
+    KVZ_LAUNCH("evict_mask", head_window_mask, mask_grid(N), TPB, 0, st, head_keep, n_heads, n_c,
+               n_sink, n_recent, mask);
   KVZ_LAUNCH("evict_offsets", head_window_offsets, 1, 1024, 0, st, head_keep, n_heads, n_c,
              window, head_offsets);
   return hipGetLastError();
@@ -307,8 +346,13 @@ hipError_t select_tokens_launch(const float* S, int64_t n_heads, int n_c, int64_
                     a.sel_ws, st);
   if (e != hipSuccess) return e;
   const int64_t N = n_heads * (int64_t)n_c;
-  KVZ_LAUNCH("evict_mask", token_broadcast_mask, mask_grid(N), TPB, 0, st, token_keep, n_heads,
-             n_c, mask);
+  if (n_c % 16 == 0 && (reinterpret_cast<uintptr_t>(token_keep) & 15u) == 0)
+    KVZ_LAUNCH("evict_mask", token_broadcast_mask16, mask_grid(N), TPB, 0, st,
+               reinterpret_cast<const uint4*>(token_keep), n_c / 16, (int)(N / 16),
+               reinterpret_cast<uint4*>(mask));
+  else
+    KVZ_LAUNCH("evict_mask", token_broadcast_mask, mask_grid(N), TPB, 0, st, token_keep, n_heads,
+               n_c, mask);
   int64_t ob = (n_heads + 1 + TPB - 1) / TPB;
   if (ob > 1024) ob = 1024;
   KVZ_LAUNCH("evict_offsets", token_offsets, (unsigned)ob, TPB, 0, st, n_heads, K_tokens,

@@ -47,7 +47,7 @@ def check_tokens(S_np, K):
 
 @pytest.mark.parametrize("ties", [False, True])
 @pytest.mark.parametrize("shape", [(1, 1), (3, 7), (8, 1000), (37, 4099), (256, 2048),
-                                   (2000, 33)])
+                                   (2000, 33), (5, 48)])
 def test_select_heads_matches_oracle(shape, ties):
     n_heads, n_c = shape
     S = _scores(shape, n_heads * 7 + n_c, ties)
@@ -58,7 +58,7 @@ def test_select_heads_matches_oracle(shape, ties):
 
 @pytest.mark.parametrize("ties", [False, True])
 @pytest.mark.parametrize("shape", [(1, 1), (3, 7), (8, 1000), (37, 4099), (2, 20000),
-                                   (300, 97)])
+                                   (300, 97), (5, 48)])
 def test_select_tokens_matches_oracle(shape, ties):
     n_heads, n_c = shape
     S = _scores(shape, n_heads * 11 + n_c, ties)
