@@ -71,3 +71,14 @@ def test_cost_model_matches_the_two_times_prefill_statement():
     # pass 2 covers exactly the context part of pass 1's logits
     a, b = bench.score_flops(wl, 2064)
     assert b == 2 * d * H * G * 2064 * n_c and a - b == 2 * d * H * G * 2064 * 2065 // 2
+
+
+def test_bench_refuses_more_than_one_gpu():
+    """bench.py runs on one GPU: any other --gpus exits with status 2 and a
+    message, before it imports torch or touches a device."""
+    import subprocess
+    import sys
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=60)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr and r.stdout == ""
