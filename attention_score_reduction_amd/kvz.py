@@ -469,10 +469,12 @@ def kvz_decode_packed(q, k_rows, v_rows, head_offsets, max_len, scale=None, out=
     k_rows/v_rows [rows][d] (head h owns head_offsets[h]..head_offsets[h+1]).
     Returns out [n_heads][G][d] fp32."""
     import torch
+    if q.dim() != 3:
+        raise ValueError("q must be [n_heads][G][d]")
     n_heads, G, d = q.shape
     if k_rows.dtype != q.dtype or v_rows.dtype != q.dtype:
         raise TypeError("q, k_rows and v_rows must share a dtype")
-    if k_rows.shape[-1] != d or v_rows.shape != k_rows.shape:
+    if k_rows.dim() != 2 or k_rows.shape[-1] != d or v_rows.shape != k_rows.shape:
         raise ValueError("k_rows/v_rows must be [rows][d] with matching shapes")
     if head_offsets.dtype != torch.int64 or head_offsets.numel() != n_heads + 1:
         raise ValueError("head_offsets must be int64 [n_heads + 1]")
@@ -481,6 +483,7 @@ def kvz_decode_packed(q, k_rows, v_rows, head_offsets, max_len, scale=None, out=
         scale = d ** -0.5
     if out is None:
         out = torch.empty(n_heads, G, d, dtype=torch.float32, device=q.device)
+    _need(out, "out", torch.float32, shape=(n_heads, G, d), device=q.device)
     if ws is None:
         ws = _ws(kvz_decode_workspace(n_heads, G, d, max_len), q.device)
     st = lib().kvz_decode_packed(dt, n_heads, G, d, int(max_len), _ptr(q, "q"),

@@ -411,3 +411,45 @@ def test_structured_select_binding_rejects(fn):
         with pytest.raises((TypeError, ValueError), match=name) as e:
             f(**kw)
         assert "device tensor" not in str(e.value)
+
+
+@pytest.mark.parametrize("case", ["q_2d", "k_1d", "v_shape", "kv_dtype", "offs_short", "offs_i32",
+                                  "out_bf16", "out_shape"])
+def test_decode_binding_rejects(case):
+    n_heads, G, d, rows = 3, 2, 64, 50
+    a = dict(q=torch.zeros(n_heads, G, d, dtype=torch.bfloat16),
+             k_rows=torch.zeros(rows, d, dtype=torch.bfloat16),
+             v_rows=torch.zeros(rows, d, dtype=torch.bfloat16),
+             head_offsets=_t(n_heads + 1, torch.int64), max_len=rows,
+             out=torch.zeros(n_heads, G, d, dtype=torch.float32))
+    if case == "q_2d":
+        a["q"] = torch.zeros(n_heads * G, d, dtype=torch.bfloat16)
+    elif case == "k_1d":
+        a["k_rows"] = torch.zeros(rows * d, dtype=torch.bfloat16)
+    elif case == "v_shape":
+        a["v_rows"] = torch.zeros(rows - 1, d, dtype=torch.bfloat16)
+    elif case == "kv_dtype":
+        a["k_rows"] = a["k_rows"].float()
+    elif case == "offs_short":
+        a["head_offsets"] = _t(n_heads, torch.int64)
+    elif case == "offs_i32":
+        a["head_offsets"] = _t(n_heads + 1, torch.int32)
+    elif case == "out_bf16":
+        a["out"] = torch.zeros(n_heads, G, d, dtype=torch.bfloat16)
+    elif case == "out_shape":
+        a["out"] = torch.zeros(n_heads, G, d - 1, dtype=torch.float32)
+    name = {"q_2d": "q", "k_1d": "k_rows", "v_shape": "v_rows", "kv_dtype": "share a dtype",
+            "offs_short": "head_offsets", "offs_i32": "head_offsets", "out_bf16": "out",
+            "out_shape": "out"}[case]
+    with pytest.raises((TypeError, ValueError), match=name) as e:
+        kvz.kvz_decode_packed(**a, ws=_t(256, torch.uint8))
+    assert "device tensor" not in str(e.value)
+
+
+def test_decode_binding_reaches_device_check_when_valid():
+    with pytest.raises(ValueError, match="device tensor"):
+        kvz.kvz_decode_packed(torch.zeros(3, 2, 64, dtype=torch.bfloat16),
+                              torch.zeros(50, 64, dtype=torch.bfloat16),
+                              torch.zeros(50, 64, dtype=torch.bfloat16), _t(4, torch.int64), 50,
+                              out=torch.zeros(3, 2, 64, dtype=torch.float32),
+                              ws=_t(256, torch.uint8))
