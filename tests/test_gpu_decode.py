@@ -99,3 +99,12 @@ def test_decode_on_compacted_cache_matches_kept_rows():
         ref[h] = ras.decode_attention(ras.bf16_to_f64(q[h:h + 1]), kk, vv,
                                       np.array([0, len(js)]), 1 / math.sqrt(d))[0]
     assert_scores_close(out.cpu().numpy(), ref, atol=1e-4, rtol=1e-3, what="decode packed")
+
+
+def test_decode_at_full_cache_length_sampled_heads():
+    """Heads as long as the 128K cache (131072 rows, d = 128, G = 4, the
+    shape the benchmark decodes), and packed-length heads around 30% of it,
+    against the oracle."""
+    lens = [131072, 39322, 131071, 40000]
+    got, ref = _case(len(lens), 4, 128, lens, "bf16", 131)
+    assert_scores_close(got, ref, atol=1e-4, rtol=1e-3, what="decode 128K-length heads")

@@ -131,3 +131,14 @@ def test_evictions_on_a_scored_cache():
     flip = np.nonzero(kt != kt_ref)[0]
     assert flip.size <= 0.001 * wl.n_ctx + 2
     assert np.all(np.abs(ts[flip] - tau_t) <= ATOL + RTOL * tau_t)
+
+
+@pytest.mark.parametrize("ties", [False, True])
+def test_evictions_at_full_cache_size(ties):
+    """The 128K LLaMA cache's score array (256 (layer, head) rows x 131072
+    tokens, the launch shapes the benchmark times): head eviction keeping 77
+    heads whole with 64 + 1024-token windows, token eviction keeping 39322
+    positions, both bit-exact against the oracle on the same scores."""
+    S = _scores((256, 131072), 4242 + int(ties), ties)
+    check_heads(S, 77, 64, 1024)
+    check_tokens(S, 39322)
