@@ -56,7 +56,7 @@ def oracle_layer_scores(gen, layer, heads, chunk_ids=None):
 # ---------------------------------------------------------------------------
 
 def pool_workers():
-    """Worker count: every host core, at most 16 (a GPU machine's CPU share)."""
+    """Worker count: every host core, at most 16 (the CPU share one GPU's host gives a process)."""
     import os
     return max(1, min(16, os.cpu_count() or 1))
 
