@@ -106,14 +106,16 @@ def test_rows_are_scipy_softmax_over_visible_prefix():
         assert np.all(P[i, n_c + i + 1:] == 0.0)
 
 
-def test_brute_force_pure_python():
-    """Tiny case by pure-Python loops with math.exp and math.fsum."""
+@pytest.mark.parametrize("row_block", [256, 2, 1])
+def test_brute_force_pure_python(row_block):
+    """Tiny case by pure-Python loops with math.exp and math.fsum; the
+    oracle's rows taken in blocks of row_block (2: a second, ragged block)."""
     H, G, n_c, n_in, d = 2, 2, 5, 3, 4
     q = _rand((H, G, n_in, d), 9)
     kc = _rand((H, n_c, d), 10)
     ki = _rand((H, n_in, d), 11)
     scale = 0.5
-    S = ras.score_layer([(q, ki)], kc, scale)
+    S = ras.score_chunk(q, kc, ki, scale, np.zeros((H, n_c)), row_block=row_block)
     for h in range(H):
         best = [0.0] * n_c
         for g in range(G):
@@ -295,12 +297,13 @@ def test_sum_mode_zero_queries_closed_form():
     np.testing.assert_allclose(S, want, rtol=1e-14)
 
 
-def test_sum_mode_brute_force_and_mass():
+@pytest.mark.parametrize("row_block", [256, 3, 1])
+def test_sum_mode_brute_force_and_mass(row_block):
     H, G, n_c, n_in, d = 1, 2, 6, 4, 5
     q = _rand((H, G, n_in, d), 62)
     kc = _rand((H, n_c, d), 63)
     ki = _rand((H, n_in, d), 64)
-    S = ras.score_layer([(q, ki)], kc, 0.4, mode="sum")[0]
+    S = ras.score_chunk(q, kc, ki, 0.4, np.zeros((H, n_c)), row_block=row_block, mode="sum")[0]
     want = [0.0] * n_c
     chunk_mass = 0.0
     for g in range(G):
@@ -435,9 +438,11 @@ def test_attention_output_single_row_is_library_attention():
         np.testing.assert_allclose(O[h, :, 0], want, rtol=1e-12, atol=1e-14)
 
 
-def test_attention_output_brute_force_pure_python():
+@pytest.mark.parametrize("row_block", [256, 2, 1])
+def test_attention_output_brute_force_pure_python(row_block):
     """Tiny case by pure-Python loops (math.exp, math.fsum), causal key set;
-    value rows differ from key rows, so a P.K or transposed contraction fails."""
+    value rows differ from key rows, so a P.K or transposed contraction fails.
+    The oracle takes the rows in blocks of row_block."""
     H, G, n_c, n_in, d, dv = 1, 2, 4, 3, 3, 2
     q = _rand((H, G, n_in, d), 91)
     kc = _rand((H, n_c, d), 92)
@@ -445,7 +450,7 @@ def test_attention_output_brute_force_pure_python():
     vc = _rand((H, n_c, dv), 94)
     vi = _rand((H, n_in, dv), 95)
     scale = 0.8
-    O = ras.chunk_attention_output(q, kc, ki, vc, vi, scale)
+    O = ras.chunk_attention_output(q, kc, ki, vc, vi, scale, row_block=row_block)
     for g in range(G):
         for i in range(n_in):
             keys = [kc[0, j] for j in range(n_c)] + [ki[0, t] for t in range(i + 1)]
