@@ -1,0 +1,67 @@
+"""The oracle's pins catch plausible mistakes: each case below plants one
+mistake in a scratch copy of oracle/ras.py (CPU only) and runs
+tests/test_oracle_pins.py against it, which must fail."""
+import os
+import shutil
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+MUTANTS = [
+    # (name, text in oracle/ras.py, replacement)
+    ("causal mask shifted by one key",
+     "invisible = t[None, :] > rows[:, None]",
+     "invisible = t[None, :] > rows[:, None] + 1"),
+    ("causal limits counted from the row block",
+     "invisible = t[None, :] > rows[:, None]",
+     "invisible = t[None, :] > (rows - rows[0])[:, None]"),
+    ("select breaks ties to the higher index",
+     "order = np.lexsort((np.arange(N), -S_flat.astype(np.float64)))",
+     "order = np.lexsort((-np.arange(N), -S_flat.astype(np.float64)))"),
+    ("select keeps K + 1",
+     "mask[order[:K]] = 1",
+     "mask[order[:K + 1]] = 1"),
+    ("tau is the (K+1)-th score",
+     "tau = float(S_flat[order[K - 1]]) if K > 0 else math.inf",
+     "tau = float(S_flat[order[min(K, N - 1)]]) if K > 0 else math.inf"),
+    ("sink window one token too long",
+     "window = (j < n_sink) | (j >= n_c - n_recent)",
+     "window = (j <= n_sink) | (j >= n_c - n_recent)"),
+    ("recent window one token too short",
+     "window = (j < n_sink) | (j >= n_c - n_recent)",
+     "window = (j < n_sink) | (j > n_c - n_recent)"),
+    ("decode without the scale",
+     "x = (q[h] @ K.T) * scale",
+     "x = (q[h] @ K.T)"),
+    ("decode weights the keys instead of the values",
+     "out[h] = p @ V",
+     "out[h] = p @ K"),
+    ("attention output over the keys",
+     "vals = np.concatenate([v_ctx[h], v_in[h]], axis=0)",
+     "vals = np.concatenate([k_ctx[h], k_in[h]], axis=0)"),
+    ("token score is the mean over heads",
+     "return np.asarray(S2d).max(axis=0)",
+     "return np.asarray(S2d).mean(axis=0)"),
+    ("head score is the sum over tokens",
+     "return np.asarray(S2d).max(axis=1)",
+     "return np.asarray(S2d).sum(axis=1)"),
+]
+
+
+@pytest.mark.parametrize("name,old,new", MUTANTS, ids=[m[0] for m in MUTANTS])
+def test_pins_fail_on_planted_mistake(tmp_path, name, old, new):
+    shutil.copytree(os.path.join(ROOT, "oracle"), tmp_path / "oracle")
+    (tmp_path / "tests").mkdir()
+    shutil.copytree(os.path.join(ROOT, "tests", "golden"), tmp_path / "tests" / "golden")
+    shutil.copy(os.path.join(ROOT, "tests", "test_oracle_pins.py"), tmp_path / "tests")
+    src = tmp_path / "oracle" / "ras.py"
+    text = src.read_text()
+    assert text.count(old) == 1, f"mutation site not unique: {name}"
+    src.write_text(text.replace(old, new))
+    r = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider",
+                        "tests/test_oracle_pins.py"], cwd=tmp_path, capture_output=True,
+                       text=True, timeout=300)
+    assert r.returncode != 0, f"the pins pass with the planted mistake: {name}\n{r.stdout[-500:]}"
