@@ -48,6 +48,24 @@ MUTANTS = [
     ("head score is the sum over tokens",
      "return np.asarray(S2d).max(axis=1)",
      "return np.asarray(S2d).sum(axis=1)"),
+    ("only the first query head of a group",
+     "        for g in range(G):\n            for r0 in range(0, n_in, row_block):\n                rows = np.arange(r0, min(n_in, r0 + row_block))\n                if mode",
+     "        for g in range(1):\n            for r0 in range(0, n_in, row_block):\n                rows = np.arange(r0, min(n_in, r0 + row_block))\n                if mode"),
+    ("score overwritten instead of a running max",
+     "np.maximum(S[h], P[:, :n_c].max(axis=0), out=S[h])",
+     "S[h] = P[:, :n_c].max(axis=0)"),
+    ("softmax over the context keys only",
+     "keys = np.concatenate([k_ctx_h, k_in_h], axis=0)",
+     "keys = np.concatenate([k_ctx_h, 0 * k_in_h - 1e300], axis=0)"),
+    ("sum aggregation takes the max",
+     "S[h] += P[:, :n_c].sum(axis=0)",
+     "S[h] += P[:, :n_c].max(axis=0)"),
+    ("compaction stores positions from 1",
+     "idx[o:o + len(js)] = js",
+     "idx[o:o + len(js)] = js + 1"),
+    ("compaction takes V rows for K",
+     "k_out[o:o + len(js)] = k_ctx[h, js]",
+     "k_out[o:o + len(js)] = v_ctx[h, js]"),
 ]
 
 
