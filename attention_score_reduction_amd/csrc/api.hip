@@ -313,8 +313,17 @@ kvz_status kvz_compact(kvz_dtype dt, int d, int n_c, int64_t head_begin, int64_t
   return e == hipSuccess ? KVZ_OK : KVZ_ERR_HIP;
 }
 
+// Both decode launches stay below 2^32 work-items: one 256-thread workgroup
+// per (head, 2048-row segment), then one d-thread workgroup per query head.
+static bool decode_grid_ok(int64_t n_heads, int G, int d, int max_len) {
+  const DecodePlan p = decode_plan(n_heads, G, d, max_len);
+  return n_heads * (int64_t)p.n_seg < (int64_t(1) << 24) &&
+         n_heads * G * (int64_t)d < (int64_t(1) << 32);
+}
+
 size_t kvz_decode_workspace(int64_t n_heads, int G, int d, int max_len) {
   if (n_heads < 1 || G < 1 || G > 8 || !head_dim_ok(d) || max_len < 1) return 0;
+  if (!decode_grid_ok(n_heads, G, d, max_len)) return 0;
   return decode_plan(n_heads, G, d, max_len).total_bytes;
 }
 
@@ -325,7 +334,8 @@ kvz_status kvz_decode_packed(kvz_dtype dt, int64_t n_heads, int G, int d, int ma
   if (dt != KVZ_BF16 && dt != KVZ_F32) return KVZ_ERR_UNSUPPORTED;
   if (!head_dim_ok(d) || G < 1 || G > 8) return KVZ_ERR_UNSUPPORTED;
   if (n_heads < 1 || max_len < 1) return KVZ_ERR_INVALID_ARG;
-  if ((int64_t)n_heads * ((max_len + 1023) / 1024) >= (int64_t(1) << 31)) return KVZ_ERR_INVALID_ARG;
+  if (!decode_grid_ok(n_heads, G, d, max_len)) return KVZ_ERR_INVALID_ARG;
+  const DecodePlan p = decode_plan(n_heads, G, d, max_len);
   if (!q || !k_rows || !v_rows || !head_offsets || !out || !ws) return KVZ_ERR_INVALID_ARG;
   if (!aligned16(q) || !aligned16(k_rows) || !aligned16(v_rows) ||
       (reinterpret_cast<uintptr_t>(head_offsets) & 7u) != 0 ||
@@ -333,7 +343,6 @@ kvz_status kvz_decode_packed(kvz_dtype dt, int64_t n_heads, int G, int d, int ma
       (reinterpret_cast<uintptr_t>(ws) & 255u) != 0)
     return KVZ_ERR_INVALID_ARG;
   if (!(scale > 0.f) || !isfinite(scale)) return KVZ_ERR_INVALID_ARG;
-  const DecodePlan p = decode_plan(n_heads, G, d, max_len);
   if (ws_bytes < p.total_bytes) return KVZ_ERR_WORKSPACE;
   clear_error();
   const hipError_t e = decode_launch(dt, p, q, k_rows, v_rows, head_offsets, scale, out, ws,

@@ -289,7 +289,8 @@ DecodePlan decode_plan(int64_t n_heads, int G, int d, int max_len) {
   p.G = G;
   p.d = d;
   p.seg_rows = SEG_ROWS;
-  p.n_seg = (max_len + p.seg_rows - 1) / p.seg_rows;
+  // 64-bit: max_len may be as large as INT_MAX
+  p.n_seg = (int)(((int64_t)max_len + p.seg_rows - 1) / p.seg_rows);
   if (p.n_seg < 1) p.n_seg = 1;
   p.total_bytes = align256((size_t)n_heads * p.n_seg * G * (d + 2) * sizeof(float));
   return p;

@@ -309,8 +309,10 @@ KVZ_API kvz_status kvz_compact(kvz_dtype dt, int d, int n_c, int64_t head_begin,
  *   max_len       host upper bound on every head's row count (rows of a head
  *                 beyond it are not read)
  *   out           device fp32 [n_heads][G][d]
- * Limits: d in {64, 128, 256}, 1 <= G <= 8.  Workspace:
- * kvz_decode_workspace() bytes (per-segment partial results).
+ * Limits: d in {64, 128, 256}, 1 <= G <= 8, n_heads * ceil(max_len / 2048)
+ * < 2^24, n_heads * G * d < 2^32 (else KVZ_ERR_INVALID_ARG, and a workspace
+ * size of 0).  Workspace: kvz_decode_workspace() bytes (per-segment partial
+ * results).
  * ---------------------------------------------------------------------- */
 KVZ_API size_t kvz_decode_workspace(int64_t n_heads, int G, int d, int max_len);
 

@@ -158,6 +158,16 @@ def test_decode_validation():
     assert f(wsb=8) == kvz.KVZ_ERR_WORKSPACE
     assert kvz.kvz_decode_workspace(256, 4, 128, 131072) > 0
     assert kvz.kvz_decode_workspace(256, 9, 128, 131072) == 0
+    # max_len near INT_MAX: 2^20 segments of 2048 rows, no int overflow
+    big = 2**31 - 1
+    assert kvz.kvz_decode_workspace(1, 1, 64, big) == 2**20 * 66 * 4
+    assert f(nh=15, G=1, d=64, ml=big, wsb=8) == kvz.KVZ_ERR_WORKSPACE
+    # grid bounds: (head, segment) workgroups < 2^24, query-head threads < 2^32
+    assert f(nh=16, G=1, d=64, ml=big) == kvz.KVZ_ERR_INVALID_ARG
+    assert kvz.kvz_decode_workspace(16, 1, 64, big) == 0
+    assert f(nh=2**21, G=8, d=256, ml=1) == kvz.KVZ_ERR_INVALID_ARG
+    assert kvz.kvz_decode_workspace(2**21, 8, 256, 1) == 0
+    assert kvz.kvz_decode_workspace(2**21 - 1, 8, 256, 1) > 0
 
 
 def test_select_validation():
