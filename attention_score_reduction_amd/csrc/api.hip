@@ -107,7 +107,8 @@ const char* kvz_status_string(kvz_status s) {
 size_t kvz_score_chunk_workspace(kvz_dtype dt, int H, int G, int n_in, int d, int n_c) {
   if (!heads_ok(H) || G < 1 || n_in < 1 || n_c < 1 || (dt != KVZ_BF16 && dt != KVZ_F32)) return 0;
   if ((long long)G * n_in > (1 << 20) || !ctx_fits(n_c, d)) return 0;
-  return score_plan(dt, H, G, n_in, d, n_c).total_bytes;
+  const ScorePlan p = score_plan(dt, H, G, n_in, d, n_c);
+  return p.fits ? p.total_bytes : 0;
 }
 
 kvz_status kvz_score_chunk_ex(kvz_dtype dt, kvz_aggregate agg, int H, int G, int d, int n_c,
@@ -127,6 +128,7 @@ kvz_status kvz_score_chunk_ex(kvz_dtype dt, kvz_aggregate agg, int H, int G, int
   if ((reinterpret_cast<uintptr_t>(ws) & 255u) != 0) return KVZ_ERR_INVALID_ARG;
   if (!(scale > 0.f) || !isfinite(scale)) return KVZ_ERR_INVALID_ARG;
   const ScorePlan p = score_plan(dt, H, G, n_in, d, n_c);
+  if (!p.fits) return KVZ_ERR_INVALID_ARG;
   if (ws_bytes < p.total_bytes) return KVZ_ERR_WORKSPACE;
   clear_error();
   const hipError_t e = score_launch(dt, agg, p, q, k_ctx, k_in, scale, S, ws,
@@ -146,7 +148,8 @@ size_t kvz_score_chunk_attn_workspace(kvz_dtype dt, int H, int G, int n_in, int 
       n_in < 1 || n_c < 1 || (long long)G * n_in > (1 << 20) || !ctx_fits(n_c, d))
     return 0;
   const ScorePlan p = score_plan(dt, H, G, n_in, d, n_c);
-  return p.total_bytes + attn_plan(dt, p).part_bytes;
+  const AttnPlan a = attn_plan(dt, p);
+  return p.fits && a.fits ? p.total_bytes + a.part_bytes : 0;
 }
 
 kvz_status kvz_score_chunk_attn(kvz_dtype dt, int H, int G, int d, int n_c, int n_prompt,
@@ -166,6 +169,7 @@ kvz_status kvz_score_chunk_attn(kvz_dtype dt, int H, int G, int d, int n_c, int 
   if (!(scale > 0.f) || !isfinite(scale)) return KVZ_ERR_INVALID_ARG;
   const ScorePlan p = score_plan(dt, H, G, n_in, d, n_c);
   const AttnPlan a = attn_plan(dt, p);
+  if (!p.fits || !a.fits) return KVZ_ERR_INVALID_ARG;
   if (ws_bytes < p.total_bytes + a.part_bytes) return KVZ_ERR_WORKSPACE;
   clear_error();
   const hipStream_t st = reinterpret_cast<hipStream_t>(stream);

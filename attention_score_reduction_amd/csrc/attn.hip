@@ -437,6 +437,7 @@ hipError_t launch3(kvz_dtype dt, const ScorePlan& p, const AttnPlan& a, const vo
 
 AttnPlan attn_plan(kvz_dtype dt, const ScorePlan& p) {
   AttnPlan a{};
+  a.fits = true;
   if (dt != KVZ_BF16) return a;  // the fp32 kernel needs no workspace of its own
   a.n_rt = (p.R + ROWS3 - 1) / ROWS3;  // row tiles holding real rows (<= R_pad / ROWS3)
   const int n_ctx_tiles = (p.n_c + KT - 1) / KT;
@@ -451,6 +452,10 @@ AttnPlan attn_plan(kvz_dtype dt, const ScorePlan& p) {
       align256((size_t)(a.n_split_ctx + 1) * p.H * p.R_pad * p.d * sizeof(float));
   a.part_bytes =
       a.opart_bytes + align256((size_t)(a.n_split_ctx + 1) * p.H * p.R_pad * sizeof(float2));
+  const int64_t nb = (int64_t)p.H * (a.n_split_ctx + 1) * a.n_rt;
+  const int64_t merge = (int64_t)p.H * p.G * p.n_in * (p.d / 4);  // one float4 per lane
+  a.fits = launch_fits((nb + kNumXcd - 1) / kNumXcd * kNumXcd, 256) &&
+           launch_fits((merge + 255) / 256, 256);
   return a;
 }
 

@@ -26,6 +26,12 @@ __device__ __forceinline__ int xcd_logical_block() {
 
 inline int xcd_padded_grid(int n) { return (n + kNumXcd - 1) / kNumXcd * kNumXcd; }
 
+// A 1-D launch of `blocks` workgroups of `threads` lanes: its work-item count
+// is a 32-bit dispatch field.
+inline bool launch_fits(int64_t blocks, int threads) {
+  return blocks >= 1 && blocks * threads <= int64_t(0xffffffff);
+}
+
 __device__ __forceinline__ uint4 ld16(const void* p) {
   return *reinterpret_cast<const uint4*>(p);
 }
@@ -81,6 +87,7 @@ struct ScorePlan {
   int n_split_ctx;      // pass-1 splits of the context keys (+1 in-chunk split)
   int tiles_per_split;  // 32-key tiles per context split
   size_t part_bytes, lse_bytes, total_bytes;
+  bool fits;  // every launch within 32-bit work-item counts and int row indices
 };
 ScorePlan score_plan(kvz_dtype dt, int H, int G, int n_in, int d, int n_c);
 hipError_t score_launch(kvz_dtype dt, kvz_aggregate agg, const ScorePlan& p, const void* q,
@@ -102,6 +109,7 @@ struct AttnPlan {
   size_t part_bytes;    // partial outputs and row (max, sum) partials, after the
                         // score workspace
   size_t opart_bytes;   // the partial outputs' share of part_bytes
+  bool fits;            // every launch within 32-bit work-item counts
 };
 AttnPlan attn_plan(kvz_dtype dt, const ScorePlan& p);
 // bf16: the whole fused call (output pass forming the row (max, sum) partials

@@ -72,6 +72,7 @@ extern "C" kvz_status kvz_score_chunk_noalloc(kvz_dtype dt, int H, int G, int d,
     return KVZ_ERR_INVALID_ARG;
   if (!(scale > 0.f) || !isfinite(scale)) return KVZ_ERR_INVALID_ARG;
   const ScorePlan p = score_plan(dt, H, G, n_in, d, n_c);
+  if (!p.fits) return KVZ_ERR_INVALID_ARG;
   if (p.total_bytes > kScratchBytes) return KVZ_ERR_WORKSPACE;
   hipError_t e = hipSuccess;
   void* ws = scratch_on_current_device(&e);

@@ -895,6 +895,16 @@ ScorePlan score_plan(kvz_dtype dt, int H, int G, int n_in, int d, int n_c) {
   }
   p.lse_bytes = align256((size_t)H * p.R_pad * sizeof(float));
   p.total_bytes = p.part_bytes + p.lse_bytes;
+  // row indices h * R_pad + r are int; the bf16 grids are XCD-padded
+  const int keys2 = d == 64 ? P2Shape<64>::KEYS : d == 128 ? P2Shape<128>::KEYS
+                                                           : P2Shape<256>::KEYS;
+  const int64_t rows_all = (int64_t)H * p.R_pad;
+  const int64_t nb1 = (int64_t)H * (p.n_split_ctx + 1) * p.n_rt;
+  const int64_t nb2 = (int64_t)H * ((n_c + keys2 - 1) / keys2);
+  p.fits = rows_all < (int64_t(1) << 31) && launch_fits((rows_all + 255) / 256, 256);
+  if (dt == KVZ_BF16)
+    p.fits = p.fits && launch_fits((nb1 + kNumXcd - 1) / kNumXcd * kNumXcd, 256) &&
+             launch_fits((nb2 + kNumXcd - 1) / kNumXcd * kNumXcd, 256);
   return p;
 }
 

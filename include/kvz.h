@@ -117,8 +117,10 @@ KVZ_API const char* kvz_build_id(void);
  * Limits: d in {64, 128, 256}; 1 <= n_in, 1 <= n_c <= 2^24 with one head's
  * keys under 2 GiB (n_c * d * 2 <= 2^31 - 1, i.e. n_c <= 4,194,303 at d=256
  * and 8,388,607 at d=128), 1 <= H <= 4096, 1 <= G,
- * G * n_in <= 2^20.  Workspace: kvz_score_chunk_workspace() bytes, 256-byte
- * aligned, device memory.
+ * G * n_in <= 2^20.  A problem too large for the launches' 32-bit
+ * work-item counts returns KVZ_ERR_INVALID_ARG (and a workspace size of 0);
+ * every problem with H * G * n_in <= 2^29 and H * n_c <= 2^31 fits.  Workspace:
+ * kvz_score_chunk_workspace() bytes, 256-byte aligned, device memory.
  * ---------------------------------------------------------------------- */
 KVZ_API size_t kvz_score_chunk_workspace(kvz_dtype dt, int H, int G, int n_in, int d, int n_c);
 
@@ -174,7 +176,9 @@ KVZ_API kvz_status kvz_score_chunk_noalloc(kvz_dtype dt, int H, int G, int d, in
  * with v_j the rows of [v_ctx[h]; v_in[h]] and p the softmax row of query
  * (h, g, i) that the scores are taken from.  bf16 inputs: p is rounded to
  * bf16 for the matrix product, sums in fp32.  All pointers device, 16-byte
- * aligned; NULL or misaligned -> KVZ_ERR_INVALID_ARG.  Workspace:
+ * aligned; NULL or misaligned -> KVZ_ERR_INVALID_ARG.  The output merge's
+ * launch adds to the score limits: every problem with also
+ * H * G * n_in * d <= 2^33 fits.  Workspace:
  * kvz_score_chunk_attn_workspace() bytes (it includes the score workspace),
  * 256-byte aligned; too small -> KVZ_ERR_WORKSPACE.
  * ---------------------------------------------------------------------- */

@@ -126,6 +126,35 @@ def test_score_attn_workspace_covers_score_workspace():
     assert _attn(wsb=need - 1) == kvz.KVZ_ERR_WORKSPACE
 
 
+def test_launch_size_limits():
+    """Problems past the launches' 32-bit work-item counts are refused before
+    any launch; the header's sufficient conditions (H*G*n_in <= 2^29,
+    H*n_c <= 2^31, and for the output H*G*n_in*d <= 2^33) always fit."""
+    ws = kvz.kvz_score_chunk_workspace
+    aws = kvz.kvz_score_chunk_attn_workspace
+    BF, F32 = kvz.KVZ_BF16, kvz.KVZ_F32
+    # rows: H * R_pad reaches 2^31 (4096 heads of 2^20 rows, 256-row tiles)
+    assert ws(BF, 4096, 1, 1 << 20, 128, 64) == 0
+    assert ws(F32, 4096, 1, 1 << 20, 128, 64) == 0
+    assert _score(H=4096, G=1, n_in=1 << 20, n_prompt=0, n_c=64) == kvz.KVZ_ERR_INVALID_ARG
+    assert _attn(H=4096, G=1, n_in=1 << 20, n_prompt=0, n_c=64) == kvz.KVZ_ERR_INVALID_ARG
+    # pass-2 grid: 4096 heads x 2^24 keys at d=64 (2^15 workgroups per head)
+    assert ws(BF, 4096, 1, 16, 64, 1 << 24) == 0
+    assert _score(H=4096, G=1, n_in=16, n_c=1 << 24, d=64) == kvz.KVZ_ERR_INVALID_ARG
+    # the sufficient conditions, at their edges and in every dtype and d
+    for dt in (BF, F32):
+        for d in (64, 128, 256):
+            assert ws(dt, 512, 1, 1 << 20, d, 64) > 0              # H*G*n_in = 2^29
+            assert ws(dt, 4096, 2, 1 << 16, d, 64) > 0             # H*G*n_in = 2^29
+            assert ws(dt, 128, 1, 16, d, min(1 << 24, ((1 << 31) - 1) // (2 * d))) > 0
+            assert ws(dt, 4096, 1, 16, d, 1 << 19) > 0             # H*n_c = 2^31
+            assert aws(dt, 4096, 1, (1 << 33) // (4096 * d), d, 64) > 0
+    # the output merge: H*G*n_in*d/4 float4 lanes past 2^32 (d=256)
+    assert ws(BF, 4096, 1, 1 << 17, 256, 64) > 0
+    assert aws(BF, 4096, 1, 1 << 17, 256, 64) == 0
+    assert _attn(H=4096, G=1, n_in=1 << 17, n_prompt=0, d=256, n_c=64) == kvz.KVZ_ERR_INVALID_ARG
+
+
 def test_score_ex_rejects_unknown_aggregation():
     L = kvz.lib()
     r = L.kvz_score_chunk_ex(0, 7, 2, 4, 128, 100, 4, 20, FAKE, FAKE, FAKE, 0.1, FAKE, FAKE,
