@@ -183,9 +183,13 @@ kvz_status kvz_score_chunk_attn(kvz_dtype dt, int H, int G, int d, int n_c, int 
   return e == hipSuccess ? KVZ_OK : KVZ_ERR_HIP;
 }
 
+// head maxima: one 1024-thread workgroup per head, so that the launch's
+// work-item count stays 32-bit
+constexpr int64_t kMaxHeadRows = int64_t(1) << 22;
+
 kvz_status kvz_head_scores(const float* S, int64_t n_heads, int n_c, float* head_score,
                            void* stream) {
-  if (n_heads < 1 || n_c < 1 || n_heads > (int64_t(1) << 31) - 1) return KVZ_ERR_INVALID_ARG;
+  if (n_heads < 1 || n_c < 1 || n_heads >= kMaxHeadRows) return KVZ_ERR_INVALID_ARG;
   if (!S || !head_score || !aligned16(S) || (reinterpret_cast<uintptr_t>(head_score) & 3u) != 0)
     return KVZ_ERR_INVALID_ARG;
   clear_error();
@@ -207,13 +211,15 @@ kvz_status kvz_token_scores(const float* S, int64_t n_heads, int n_c, float* tok
 
 size_t kvz_select_heads_workspace(int64_t n_heads, int n_c) {
   if (n_heads < 1 || n_c < 1 || n_heads * (int64_t)n_c >= (int64_t(1) << 31)) return 0;
+  if (n_heads >= kMaxHeadRows) return 0;
   return agg_select_workspace(n_heads);
 }
 
 kvz_status kvz_select_heads(const float* S, int64_t n_heads, int n_c, int64_t K_heads,
                             int n_sink, int n_recent, uint8_t* mask, int64_t* head_offsets,
                             uint8_t* head_keep, void* ws, size_t ws_bytes, void* stream) {
-  if (n_heads < 1 || n_c < 1 || n_heads * (int64_t)n_c >= (int64_t(1) << 31))
+  if (n_heads < 1 || n_c < 1 || n_heads * (int64_t)n_c >= (int64_t(1) << 31) ||
+      n_heads >= kMaxHeadRows)
     return KVZ_ERR_INVALID_ARG;
   if (K_heads < 0 || K_heads > n_heads || n_sink < 0 || n_recent < 0) return KVZ_ERR_INVALID_ARG;
   if (!S || !mask || !head_offsets || !head_keep || !ws) return KVZ_ERR_INVALID_ARG;

@@ -338,7 +338,7 @@ hipError_t select_tokens_launch(const float* S, int64_t n_heads, int n_c, int64_
                                 uint8_t* mask, int64_t* head_offsets, uint8_t* token_keep,
                                 void* ws, hipStream_t st) {
   const AggWs a = carve_agg(n_c, ws);
-  KVZ_LAUNCH("token_scores", token_max, (unsigned)((n_c + 255) / 256), TPB, 0, st, S,
+  KVZ_LAUNCH("token_scores", token_max, (unsigned)(((int64_t)n_c + 255) / 256), TPB, 0, st, S,
              n_heads, n_c, a.agg);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
@@ -368,7 +368,7 @@ hipError_t head_scores_launch(const float* S, int64_t n_heads, int n_c, float* o
 
 hipError_t token_scores_launch(const float* S, int64_t n_heads, int n_c, float* out,
                                hipStream_t st) {
-  KVZ_LAUNCH("token_scores", token_max, (unsigned)((n_c + 255) / 256), TPB, 0, st, S, n_heads,
+  KVZ_LAUNCH("token_scores", token_max, (unsigned)(((int64_t)n_c + 255) / 256), TPB, 0, st, S, n_heads,
              n_c, out);
   return hipGetLastError();
 }

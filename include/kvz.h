@@ -198,6 +198,7 @@ KVZ_API kvz_status kvz_score_chunk_attn(kvz_dtype dt, int H, int G, int d, int n
  * heads):
  *   token_score[j] = max over h of S[h][j]       (device fp32 [n_c])
  * S: device fp32 [n_heads][n_c], 16-byte aligned.  No workspace.
+ * Limits: n_heads < 2^22 for the head maxima.
  * ---------------------------------------------------------------------- */
 KVZ_API kvz_status kvz_head_scores(const float* S, int64_t n_heads, int n_c, float* head_score,
                                    void* stream);
@@ -221,7 +222,8 @@ KVZ_API kvz_status kvz_token_scores(const float* S, int64_t n_heads, int n_c, fl
  *   head_offsets device int64 [n_heads + 1], out (exclusive scan of the
  *                per-head kept counts).
  *   head_keep    device uint8 [n_heads], out: 1 = head kept whole.
- * 0 <= K_heads <= n_heads, n_sink >= 0, n_recent >= 0, n_heads * n_c < 2^31.
+ * 0 <= K_heads <= n_heads < 2^22, n_sink >= 0, n_recent >= 0,
+ * n_heads * n_c < 2^31.
  * Workspace: kvz_select_heads_workspace() bytes, 256-byte aligned.
  *
  * kvz_select_tokens -- token-level eviction (blog 4.3.3: one score per

@@ -171,6 +171,16 @@ def test_head_token_validation():
     assert L.kvz_token_scores(FAKE, 4, 10, None, None) == kvz.KVZ_ERR_INVALID_ARG
 
 
+def test_head_maxima_head_count_limit():
+    # one 1024-thread workgroup per head: n_heads < 2^22 keeps the launch 32-bit
+    L = kvz.lib()
+    assert L.kvz_head_scores(FAKE, 1 << 22, 1, FAKE, None) == kvz.KVZ_ERR_INVALID_ARG
+    assert kvz.kvz_select_heads_workspace((1 << 22) - 1, 1) > 0
+    assert kvz.kvz_select_heads_workspace(1 << 22, 1) == 0
+    r = L.kvz_select_heads(FAKE, 1 << 22, 1, 1, 0, 0, FAKE, FAKE, FAKE, FAKE, 1 << 30, None)
+    assert r == kvz.KVZ_ERR_INVALID_ARG
+
+
 def test_decode_validation():
     L = kvz.lib()
     f = lambda dt=0, nh=4, G=4, d=128, ml=100, q=FAKE, off=FAKE, out=FAKE, sc=0.1, ws=FAKE, wsb=1 << 30: \
