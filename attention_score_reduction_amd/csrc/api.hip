@@ -265,9 +265,14 @@ int64_t kvz_keep_count(int64_t N, double r) {
   return (int64_t)k;
 }
 
+// the mask and fix-up passes launch one 256-thread workgroup per tile of a
+// head's scores: fewer than 2^24 tiles keeps their work-item counts 32-bit
+constexpr int64_t kMaxSelectTiles = int64_t(1) << 24;
+
 size_t kvz_select_workspace(int64_t n_heads, int n_c) {
   if (n_heads < 1 || n_c < 1 || n_heads * (int64_t)n_c >= (int64_t(1) << 31)) return 0;
-  return select_plan(n_heads, n_c).total_bytes;
+  const SelectPlan p = select_plan(n_heads, n_c);
+  return p.n_tiles < kMaxSelectTiles ? p.total_bytes : 0;
 }
 
 kvz_status kvz_select_threshold(const float* S, int64_t n_heads, int n_c, int64_t K,
@@ -283,6 +288,7 @@ kvz_status kvz_select_threshold(const float* S, int64_t n_heads, int n_c, int64_
       (reinterpret_cast<uintptr_t>(ws) & 255u) != 0)
     return KVZ_ERR_INVALID_ARG;
   const SelectPlan p = select_plan(n_heads, n_c);
+  if (p.n_tiles >= kMaxSelectTiles) return KVZ_ERR_INVALID_ARG;
   if (ws_bytes < p.total_bytes) return KVZ_ERR_WORKSPACE;
   clear_error();
   const hipError_t e = select_launch(p, S, K, mask, head_offsets, tau_out, ws,

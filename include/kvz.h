@@ -266,7 +266,9 @@ KVZ_API int64_t kvz_keep_count(int64_t N, double r);
  * Exactly K entries are kept: every score > tau, then the scores equal to tau
  * in ascending flat index (l*H + h)*n_c + j until K is reached.  No
  * device-to-host synchronisation happens.
- * Limits: n_heads * n_c < 2^31.  Workspace: kvz_select_workspace() bytes.
+ * Limits: n_heads * n_c < 2^31 and n_heads * ceil(n_c / 4096) < 2^24 (else
+ * KVZ_ERR_INVALID_ARG and a workspace size of 0).  Workspace:
+ * kvz_select_workspace() bytes.
  * ---------------------------------------------------------------------- */
 KVZ_API size_t kvz_select_workspace(int64_t n_heads, int n_c);
 

@@ -52,6 +52,12 @@ def test_workspace_queries():
     assert kvz.kvz_select_workspace(256, 131072) > 0
     assert kvz.kvz_select_workspace(0, 10) == 0
     assert kvz.kvz_select_workspace(1 << 20, 1 << 12) == 0  # N >= 2^31
+    # 2^24 mask tiles (one 256-thread workgroup each): past the 32-bit launch
+    assert kvz.kvz_select_workspace((1 << 24) - 1, 1) > 0
+    assert kvz.kvz_select_workspace(1 << 24, 1) == 0
+    assert kvz.kvz_select_workspace(1 << 24, 64) == 0     # N = 2^30, 2^24 tiles
+    r = kvz.lib().kvz_select_threshold(FAKE, 1 << 24, 64, 1, FAKE, FAKE, FAKE, FAKE, 1 << 40, None)
+    assert r == kvz.KVZ_ERR_INVALID_ARG
     assert kvz.kvz_compact_workspace(8, 131072) > 0
     assert kvz.kvz_compact_workspace(0, 1) == 0
 
