@@ -709,7 +709,10 @@ __global__ __launch_bounds__(64) void score_pass1_f32(const float* __restrict__ 
   const int i = r / G, g = r - (r / G) * G;
   for (int k = 0; k < D; ++k)
     ldq[k][tid] = (r < R) ? q[((size_t)(h * G + g) * n_in + i) * D + k] : 0.f;
-  float m = kNegBig, l = 0.f;
+  // one thread sums a row's terms over every key it sees (up to ~2^24):
+  // compensated (Kahan) summation keeps the terms far below the running
+  // sum, which a plain fp32 sum would drop, in the total
+  float m = kNegBig, l = 0.f, c = 0.f;
   const int n_ctx_tiles = (n_c + KT - 1) / KT;
   const int imax = (min(R, (int)(blockIdx.x + 1) * 64) - 1) / G;
   const int n_tiles = n_ctx_tiles + imax / KT + 1;
@@ -732,7 +735,16 @@ __global__ __launch_bounds__(64) void score_pass1_f32(const float* __restrict__ 
       for (int k = 0; k < D; ++k) dot = fmaf(ldq[k][tid], ldk[kk][k], dot);
       const float x = dot * cl2;
       const float mn = fmaxf(m, x);
-      l = l * exp2f(m - mn) + exp2f(x - mn);
+      const float e = exp2f(x - mn), a = exp2f(m - mn);
+      {
+#pragma clang fp contract(off)  // each step rounded on its own, as the compensation needs
+        l *= a;
+        c *= a;
+        const float y = e - c;
+        const float t = l + y;
+        c = (t - l) - y;
+        l = t;
+      }
       m = mn;
     }
   }
@@ -755,6 +767,7 @@ __global__ __launch_bounds__(64) void score_pass2_f32(const float* __restrict__ 
   for (int k = 0; k < D; ++k)
     ldk[k][tid] = (j < n_c) ? kc[((size_t)h * n_c + j) * D + k] : 0.f;
   float mx = MODE == 1 ? 0.f : -INFINITY;
+  float cmp = 0.f;  // sum mode: Kahan compensation of mx (up to 2^20 rows)
   for (int r0 = 0; r0 < R; r0 += 32) {
     __syncthreads();
     for (int e = tid; e < 32 * D; e += 64) {
@@ -772,8 +785,18 @@ __global__ __launch_bounds__(64) void score_pass2_f32(const float* __restrict__ 
       float dot = 0.f;
       for (int k = 0; k < D; ++k) dot = fmaf(ldq[rr][k], ldk[k][tid], dot);
       if (MODE == 0) mx = fmaxf(mx, dot * cl2 - ldl[rr]);
-      else if (MODE == 1) mx += exp2f(dot * cl2 - ldl[rr]);
-      else mx = fmaxf(mx, dot);
+      else if (MODE == 1) {
+        const float e = exp2f(dot * cl2 - ldl[rr]);
+        {
+#pragma clang fp contract(off)
+          const float y = e - cmp;
+          const float t = mx + y;
+          cmp = (t - mx) - y;
+          mx = t;
+        }
+      } else {
+        mx = fmaxf(mx, dot);
+      }
     }
   }
   if (j < n_c) {
