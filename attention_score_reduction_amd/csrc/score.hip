@@ -491,11 +491,21 @@ __global__ __launch_bounds__(256) void score_combine(const float2* __restrict__ 
   float M = kNegBig;
 #pragma unroll 8
   for (int s = 0; s < splits; ++s) M = fmaxf(M, p[(size_t)s * R_pad].x);
-  float L = 0.f;
+  // compensated (Kahan) sum over the splits: with thousands of splits, one
+  // of them can hold nearly all of the row's weight while the others each
+  // add less than an ulp of it
+  float L = 0.f, c = 0.f;
 #pragma unroll 8
   for (int s = 0; s < splits; ++s) {
     const float2 v = p[(size_t)s * R_pad];
-    L += v.y * exp2f(v.x - M);
+    const float term = v.y * exp2f(v.x - M);
+    {
+#pragma clang fp contract(off)
+      const float y = term - c;
+      const float t = L + y;
+      c = (t - L) - y;
+      L = t;
+    }
   }
   lse2[idx] = (M + log2f(L)) * mul;
 }
