@@ -601,16 +601,20 @@ __device__ __forceinline__ void p2_block(const P2Args& args, int lb, int tid) {
   };
 
   const float init = MODE == 1 ? 0.f : -INFINITY;
-  float acc[NT];
+  // sum mode: a key's sum runs over every query row (up to 2^20); each key
+  // tile's terms are summed on their own and folded into acc with Kahan
+  // compensation (comp), so that small terms are not lost against the total
+  float acc[NT], comp[NT];
 #pragma unroll
-  for (int t = 0; t < NT; ++t) acc[t] = init;
+  for (int t = 0; t < NT; ++t) acc[t] = init, comp[t] = 0.f;
 
   // epilogue of one key tile: elements 2p, 2p+1 for p in [p0, p1).  MODE 0
   // and 2 need only a running max: for MODE 0 the MFMA accumulator starts at
   // -lse2/(scale log2 e) of its row, so its output is already the row's
   // log-probability in dot-product units, and the scaling waits until after
   // the max (it is positive).
-  auto epilogue = [&](const f32x16& c, const float4 (&L)[4], int t, int p0, int p1) {
+  // (sum mode: into the tile sum ts instead of acc)
+  auto epilogue = [&](const f32x16& c, const float4 (&L)[4], float& ts, int t, int p0, int p1) {
 #pragma unroll
     for (int pr = p0; pr < p1; ++pr) {
       const int v = 2 * pr;
@@ -620,8 +624,17 @@ __device__ __forceinline__ void p2_block(const P2Args& args, int lb, int tid) {
       } else {
         const float4 L4 = L[v >> 2];
         const float l0 = (v & 3) == 0 ? L4.x : L4.z, l1 = (v & 3) == 0 ? L4.y : L4.w;
-        acc[t] += fast_exp2(fmaf(x0, cl2, -l0)) + fast_exp2(fmaf(x1, cl2, -l1));
+        ts += fast_exp2(fmaf(x0, cl2, -l0)) + fast_exp2(fmaf(x1, cl2, -l1));
       }
+    }
+  };
+  auto fold = [&](float ts, int t) {
+    if constexpr (MODE == 1) {
+#pragma clang fp contract(off)
+      const float y = ts - comp[t];
+      const float s = acc[t] + y;
+      comp[t] = (s - acc[t]) - y;
+      acc[t] = s;
     }
   };
 
@@ -655,6 +668,7 @@ __device__ __forceinline__ void p2_block(const P2Args& args, int lb, int tid) {
     } else {
       z = f32x16{};  // sum: padding rows carry lse = +inf and add 0
     }
+    float ts[NT] = {};
     __builtin_amdgcn_sched_barrier(0);
     // MFMAs of key tile t, each followed by a share of key tile t-1's epilogue
 #pragma unroll
@@ -663,11 +677,13 @@ __device__ __forceinline__ void p2_block(const P2Args& args, int lb, int tid) {
       for (int ks = 0; ks < KS; ++ks) {
         c[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[ks], kr[t][ks], ks == 0 ? z : c[t], 0, 0,
                                                        0);
-        if (t > 0) epilogue(c[t - 1], L, t - 1, ks * 8 / KS, (ks + 1) * 8 / KS);
+        if (t > 0) epilogue(c[t - 1], L, ts[t - 1], t - 1, ks * 8 / KS, (ks + 1) * 8 / KS);
         __builtin_amdgcn_sched_barrier(0);
       }
+      if (t > 0) fold(ts[t - 1], t - 1);
     }
-    epilogue(c[NT - 1], L, NT - 1, 0, 8);
+    epilogue(c[NT - 1], L, ts[NT - 1], NT - 1, 0, 8);
+    fold(ts[NT - 1], NT - 1);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
   };

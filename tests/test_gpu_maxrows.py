@@ -89,6 +89,28 @@ def test_scores_at_the_row_limit(dtype):
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_sum_aggregation_at_the_row_limit(dtype):
+    """Sum over all 2^20 rows: the zero rows give every context key
+    sum over g, i of 1 / (n_c + i + 1) (a harmonic sum, about 104 here), each
+    planted row replaces its zero-row term by its probability on the key."""
+    arrs = _inputs(dtype)
+    scale = 1.0 / math.sqrt(D)
+    harmonic = G * sum(1.0 / (N_C + i + 1) for i in range(N_IN))
+    ref = np.full((H, N_C), harmonic)
+    for g, i, _ in PLANTED:
+        q1, kc1, kin1, _, _ = _row_problem(*arrs, dtype, g, i)
+        S1 = np.zeros((H, kc1.shape[1]))
+        ras.score_chunk(q1, kc1, kin1, scale, S1, mode="sum")
+        ref += S1[:, :N_C] - 1.0 / (N_C + i + 1)
+    q, kc, kin = (to_dev(x, dtype) for x in arrs[:3])
+    S = torch.zeros(H, N_C, dtype=torch.float32, device="cuda")
+    kvz.kvz_score_chunk_ex(q, kc, kin, S, N_PROMPT, "sum", scale)
+    torch.cuda.synchronize()
+    assert_scores_close(S.cpu().numpy(), ref, atol=1e-6, rtol=1e-5,
+                        what=f"sum S {dtype} 2^20 rows")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
 def test_attention_output_at_the_row_limit(dtype):
     arrs = _inputs(dtype)
     scale = 1.0 / math.sqrt(D)
