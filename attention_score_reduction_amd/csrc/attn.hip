@@ -331,23 +331,16 @@ __global__ __launch_bounds__(256) void attn_reduce(const float* __restrict__ opa
   // compensated (Kahan) sums over the splits, as in the score pass's merge
   float L = 0.f, cL = 0.f;
   float a[4] = {0.f, 0.f, 0.f, 0.f}, ca[4] = {0.f, 0.f, 0.f, 0.f};
-  auto kahan = [](float& sum, float& comp, float term) {
-#pragma clang fp contract(off)
-    const float y = term - comp;
-    const float t = sum + y;
-    comp = (t - sum) - y;
-    sum = t;
-  };
   for (int s = 0; s < splits; ++s) {
     const float2 v2 = ml[(size_t)s * R_pad];
     const float w = fast_exp2(v2.x - M);
-    kahan(L, cL, v2.y * w);
+    kahan_add(L, cL, v2.y * w);
     const float4 v =
         *reinterpret_cast<const float4*>(opart + (((size_t)s * H + h) * R_pad + r) * D + 4 * c4);
-    kahan(a[0], ca[0], w * v.x);
-    kahan(a[1], ca[1], w * v.y);
-    kahan(a[2], ca[2], w * v.z);
-    kahan(a[3], ca[3], w * v.w);
+    kahan_add(a[0], ca[0], w * v.x);
+    kahan_add(a[1], ca[1], w * v.y);
+    kahan_add(a[2], ca[2], w * v.z);
+    kahan_add(a[3], ca[3], w * v.w);
   }
   const float4 acc = make_float4(a[0], a[1], a[2], a[3]);
   const float inv = 1.0f / L;

@@ -41,6 +41,17 @@ __device__ __forceinline__ bf16x8 as_bf16x8(uint4 u) {
 }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Compensated (Kahan) accumulation: sum += term, with the rounding error of
+// each step carried in comp, so that terms far below the running sum still
+// count.  Contraction is off: every step must round on its own.
+__device__ __forceinline__ void kahan_add(float& sum, float& comp, float term) {
+#pragma clang fp contract(off)
+  const float y = term - comp;
+  const float t = sum + y;
+  comp = (t - sum) - y;
+  sum = t;
+}
 __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
 
 // Word 3 of a raw buffer resource on gfx9-family parts: 32-bit data format

@@ -242,7 +242,9 @@ __global__ __launch_bounds__(D) void decode_combine(const float* __restrict__ pa
   M = red[0];
 #pragma unroll
   for (int w = 1; w < NWV; ++w) M = fmaxf(M, red[w]);
-  float L = 0.f, A = 0.f;
+  // compensated sums over the segments (a long head has thousands, and one
+  // of them may hold nearly all of the weight)
+  float L = 0.f, A = 0.f, cL = 0.f, cA = 0.f;
   for (int s0 = 0; s0 < nv; s0 += U) {
     float m[U], l[U], a[U];
 #pragma unroll
@@ -256,8 +258,8 @@ __global__ __launch_bounds__(D) void decode_combine(const float* __restrict__ pa
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const float f = exp2f(m[u] - M);
-      L += l[u] * f;
-      A += a[u] * f;
+      kahan_add(L, cL, l[u] * f);
+      kahan_add(A, cA, a[u] * f);
     }
   }
   out[(h * G + g) * D + dd] = nv > 0 ? A / L : 0.f;

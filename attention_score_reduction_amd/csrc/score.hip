@@ -498,14 +498,7 @@ __global__ __launch_bounds__(256) void score_combine(const float2* __restrict__ 
 #pragma unroll 8
   for (int s = 0; s < splits; ++s) {
     const float2 v = p[(size_t)s * R_pad];
-    const float term = v.y * exp2f(v.x - M);
-    {
-#pragma clang fp contract(off)
-      const float y = term - c;
-      const float t = L + y;
-      c = (t - L) - y;
-      L = t;
-    }
+    kahan_add(L, c, v.y * exp2f(v.x - M));
   }
   lse2[idx] = (M + log2f(L)) * mul;
 }
@@ -629,13 +622,7 @@ __device__ __forceinline__ void p2_block(const P2Args& args, int lb, int tid) {
     }
   };
   auto fold = [&](float ts, int t) {
-    if constexpr (MODE == 1) {
-#pragma clang fp contract(off)
-      const float y = ts - comp[t];
-      const float s = acc[t] + y;
-      comp[t] = (s - acc[t]) - y;
-      acc[t] = s;
-    }
+    if constexpr (MODE == 1) kahan_add(acc[t], comp[t], ts);
   };
 
   // one query tile: read this tile's operands from LDS, start the copy of the
@@ -761,16 +748,10 @@ __global__ __launch_bounds__(64) void score_pass1_f32(const float* __restrict__ 
       for (int k = 0; k < D; ++k) dot = fmaf(ldq[k][tid], ldk[kk][k], dot);
       const float x = dot * cl2;
       const float mn = fmaxf(m, x);
-      const float e = exp2f(x - mn), a = exp2f(m - mn);
-      {
-#pragma clang fp contract(off)  // each step rounded on its own, as the compensation needs
-        l *= a;
-        c *= a;
-        const float y = e - c;
-        const float t = l + y;
-        c = (t - l) - y;
-        l = t;
-      }
+      const float a = exp2f(m - mn);
+      l *= a;
+      c *= a;
+      kahan_add(l, c, exp2f(x - mn));
       m = mn;
     }
   }
@@ -811,18 +792,8 @@ __global__ __launch_bounds__(64) void score_pass2_f32(const float* __restrict__ 
       float dot = 0.f;
       for (int k = 0; k < D; ++k) dot = fmaf(ldq[rr][k], ldk[k][tid], dot);
       if (MODE == 0) mx = fmaxf(mx, dot * cl2 - ldl[rr]);
-      else if (MODE == 1) {
-        const float e = exp2f(dot * cl2 - ldl[rr]);
-        {
-#pragma clang fp contract(off)
-          const float y = e - cmp;
-          const float t = mx + y;
-          cmp = (t - mx) - y;
-          mx = t;
-        }
-      } else {
-        mx = fmaxf(mx, dot);
-      }
+      else if (MODE == 1) kahan_add(mx, cmp, exp2f(dot * cl2 - ldl[rr]));
+      else mx = fmaxf(mx, dot);
     }
   }
   if (j < n_c) {
