@@ -160,3 +160,46 @@ def check_selection_end_to_end(s_gpu, s_ref, K, n_heads, n_c, kc_all, vc_all, dt
     assert near.all(), "a disagreement lies outside the score tolerance of tau"
     del torch
     return agree
+
+
+# ---------------------------------------------------------------------------
+# selection of periodic scores in closed form (scores v(f) = (f mod P) / P of
+# the flat index f): the counts of each value are known, so the exact top-K
+# with ties in ascending flat order has a closed form at any size
+# ---------------------------------------------------------------------------
+
+PERIOD = 1009
+
+
+def periodic_scores(f):
+    """fp32 scores of flat indices f (any integer array)."""
+    return ((np.asarray(f) % PERIOD).astype(np.float32) / np.float32(PERIOD)).astype(np.float32)
+
+
+def periodic_select_params(N, K):
+    """(r_star, need): the K-th largest score is residue r_star, and the first
+    `need` entries of that residue in flat order are kept (K >= 1)."""
+    full, rem = divmod(N, PERIOD)
+    above = 0
+    for r in range(PERIOD - 1, -1, -1):
+        c = full + (1 if r < rem else 0)
+        if above + c >= K:
+            return r, K - above
+        above += c
+    raise ValueError("K > N")
+
+
+def periodic_kept_before(X, r_star, need):
+    """Kept entries with flat index < X (X an int64 array)."""
+    X = np.asarray(X, np.int64)
+    full, rem = np.divmod(X, PERIOD)
+    greater = full * (PERIOD - 1 - r_star) + np.maximum(0, rem - (r_star + 1))
+    ties = np.where(X <= r_star, 0, (X - r_star - 1) // PERIOD + 1)
+    return greater + np.minimum(ties, need)
+
+
+def periodic_mask(f0, f1, r_star, need):
+    """Expected mask bytes of flat indices f0 .. f1-1."""
+    f = np.arange(f0, f1, dtype=np.int64)
+    r = f % PERIOD
+    return ((r > r_star) | ((r == r_star) & (f < r_star + need * PERIOD))).astype(np.uint8)

@@ -9,7 +9,8 @@ import pytest
 from attention_score_reduction_amd import kvz
 from attention_score_reduction_amd.inputs import WORKLOADS, HostGen, Workload
 from oracle import ras
-from tests.helpers import bits_of, check_selection_end_to_end, oracle_layer_scores, to_dev
+from tests.helpers import (PERIOD, bits_of, check_selection_end_to_end, oracle_layer_scores,
+                           periodic_kept_before, periodic_mask, periodic_select_params, to_dev)
 
 pytestmark = pytest.mark.gpu
 
@@ -91,6 +92,34 @@ def test_select_full_size_scores():
     S[7, :5000] = S[7, 0]
     K = kvz.kvz_keep_count(S.size, 0.3)
     check_select(S, K)
+
+
+def test_select_at_the_size_limit():
+    """2,147,467,264 scores (16384 heads x 131071, just under 2^31 and not a
+    multiple of 4 per head), periodic values (f mod P) / P of the flat index,
+    so the exact top-K has a closed form (pinned against the oracle's
+    selection in the oracle tests): ties split at the K-th value across every
+    tile and head."""
+    n_heads, n_c = 16384, 131071
+    N = n_heads * n_c
+    assert N < 1 << 31
+    K = kvz.kvz_keep_count(N, 0.3)
+    f = torch.arange(N, dtype=torch.int32, device="cuda")
+    S = torch.remainder(f, PERIOD).to(torch.float32).div_(PERIOD).view(n_heads, n_c)
+    del f
+    mask, offs, tau = kvz.kvz_select_threshold(S, K)
+    torch.cuda.synchronize()
+    del S
+    r_star, need = periodic_select_params(N, K)
+    assert float(tau.cpu()[0]) == float(np.float32(r_star) / np.float32(PERIOD))
+    want_offs = periodic_kept_before(np.arange(n_heads + 1, dtype=np.int64) * n_c, r_star, need)
+    assert np.array_equal(offs.cpu().numpy(), want_offs)
+    step = 1 << 27
+    for f0 in range(0, N, step):
+        f1 = min(N, f0 + step)
+        got = mask[f0:f1].cpu().numpy()
+        want = periodic_mask(f0, f1, r_star, need)
+        assert np.array_equal(got, want), f"mask differs at {f0 + np.nonzero(got != want)[0][:5]}"
 
 
 def _compact_case(wl, dtype, K_ratio, per_layer, mask_offset=0):

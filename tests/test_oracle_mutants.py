@@ -69,17 +69,33 @@ MUTANTS = [
 ]
 
 
-@pytest.mark.parametrize("name,old,new", MUTANTS, ids=[m[0] for m in MUTANTS])
-def test_pins_fail_on_planted_mistake(tmp_path, name, old, new):
+def _run_pins(tmp_path, old=None, new=None):
+    """Run the pin suite on a scratch copy of the oracle, with `old`
+    replaced by `new` in oracle/ras.py when given."""
     shutil.copytree(os.path.join(ROOT, "oracle"), tmp_path / "oracle")
     (tmp_path / "tests").mkdir()
     shutil.copytree(os.path.join(ROOT, "tests", "golden"), tmp_path / "tests" / "golden")
-    shutil.copy(os.path.join(ROOT, "tests", "test_oracle_pins.py"), tmp_path / "tests")
-    src = tmp_path / "oracle" / "ras.py"
-    text = src.read_text()
-    assert text.count(old) == 1, f"mutation site not unique: {name}"
-    src.write_text(text.replace(old, new))
-    r = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider",
-                        "tests/test_oracle_pins.py"], cwd=tmp_path, capture_output=True,
-                       text=True, timeout=300)
+    for f in ("test_oracle_pins.py", "helpers.py"):
+        shutil.copy(os.path.join(ROOT, "tests", f), tmp_path / "tests")
+    if old is not None:
+        src = tmp_path / "oracle" / "ras.py"
+        text = src.read_text()
+        assert text.count(old) == 1, f"mutation site not unique: {old}"
+        src.write_text(text.replace(old, new))
+    return subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider",
+                           "tests/test_oracle_pins.py"], cwd=tmp_path, capture_output=True,
+                          text=True, timeout=300)
+
+
+def test_pins_pass_on_the_unchanged_copy(tmp_path):
+    # the control: the scratch setup itself passes, so each failure below
+    # comes from its planted mistake
+    r = _run_pins(tmp_path)
+    assert r.returncode == 0, r.stdout[-800:]
+
+
+@pytest.mark.parametrize("name,old,new", MUTANTS, ids=[m[0] for m in MUTANTS])
+def test_pins_fail_on_planted_mistake(tmp_path, name, old, new):
+    r = _run_pins(tmp_path, old, new)
     assert r.returncode != 0, f"the pins pass with the planted mistake: {name}\n{r.stdout[-500:]}"
+    assert "ImportError" not in r.stdout and "ModuleNotFoundError" not in r.stdout, r.stdout[-800:]

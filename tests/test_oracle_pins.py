@@ -241,6 +241,22 @@ def test_select_matches_brute_force_with_ties(seed):
             assert tau == math.inf
 
 
+@pytest.mark.parametrize("n_heads,n_c,ratio", [(7, 1000, 0.3), (3, 4099, 0.5), (1, 2018, 0.001),
+                                                (5, 1009, 1.0)])
+def test_select_periodic_scores_closed_form(n_heads, n_c, ratio):
+    """Scores (f mod P) / P of the flat index: each value's count is known,
+    so the kept set, tau and the head offsets have a closed form."""
+    from tests.helpers import (PERIOD, periodic_kept_before, periodic_mask, periodic_scores,
+                               periodic_select_params)
+    N = n_heads * n_c
+    K = ras.keep_count(N, ratio)
+    mask, offs, tau = ras.select(periodic_scores(np.arange(N)), n_heads, n_c, K)
+    r_star, need = periodic_select_params(N, K)
+    assert np.array_equal(mask, periodic_mask(0, N, r_star, need))
+    assert np.array_equal(offs, periodic_kept_before(np.arange(n_heads + 1) * n_c, r_star, need))
+    assert tau == float(np.float32(r_star) / np.float32(PERIOD))
+
+
 def test_select_nonuniform_budgets():
     """One global threshold gives per-head budgets that follow each head's
     scores (atlas summary, Measured effects: non-uniform head budgets)."""
