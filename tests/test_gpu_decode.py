@@ -8,7 +8,7 @@ import pytest
 from attention_score_reduction_amd import kvz
 from attention_score_reduction_amd.inputs import bf16_bits
 from oracle import ras
-from tests.helpers import assert_scores_close, to_dev
+from tests.helpers import assert_scores_close, bits_of, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -108,3 +108,27 @@ def test_decode_at_full_cache_length_sampled_heads():
     lens = [131072, 39322, 131071, 40000]
     got, ref = _case(len(lens), 4, 128, lens, "bf16", 131)
     assert_scores_close(got, ref, atol=1e-4, rtol=1e-3, what="decode 128K-length heads")
+
+
+def test_decode_long_peaked_head():
+    """One head of 4,194,304 rows (2048 segments) whose query heads each put
+    almost all of their weight on one key (the first row, the last row, the
+    first row of a segment, a middle row), plus a zero query (the mean of
+    all values): the merge over 2048 segments must keep the other
+    segments' small shares.  Held to 1e-5 + 1e-5 |ref|."""
+    n = 1 << 22
+    d, G = 128, 5
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(4242)
+    k = torch.randn(n, d, generator=gen, device="cuda").to(torch.bfloat16)
+    v = torch.randn(n, d, generator=gen, device="cuda").to(torch.bfloat16)
+    q = torch.zeros(1, G, d, dtype=torch.bfloat16, device="cuda")
+    for g, t in enumerate([0, n - 1, 2048 * 1000, n // 2 + 7]):
+        q[0, g] = (2.3 * k[t].float()).to(torch.bfloat16)
+    offs = torch.tensor([0, n], dtype=torch.int64, device="cuda")
+    scale = 1 / math.sqrt(d)
+    out = kvz.kvz_decode_packed(q, k, v, offs, n, scale)
+    torch.cuda.synchronize()
+    f64 = lambda x: ras.to_f64(bits_of(x), "bf16")
+    ref = ras.decode_attention(f64(q), f64(k), f64(v), offs.cpu().numpy(), scale)
+    assert_scores_close(out.cpu().numpy(), ref, atol=1e-5, rtol=1e-5, what="decode 4M peaked")
