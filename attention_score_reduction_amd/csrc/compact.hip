@@ -182,7 +182,7 @@ CompactPlan compact_plan(int64_t head_count, int n_c) {
   CompactPlan p{};
   p.head_count = head_count;
   p.n_c = n_c;
-  p.tiles_per_head = (n_c + TILE - 1) / TILE;
+  p.tiles_per_head = (int)(((int64_t)n_c + TILE - 1) / TILE);  // n_c may be INT_MAX
   p.n_tiles = head_count * p.tiles_per_head;
   p.total_bytes = align256((size_t)p.n_tiles * sizeof(int64_t));
   return p;

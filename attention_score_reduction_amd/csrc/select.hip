@@ -595,7 +595,7 @@ SelectPlan select_plan(int64_t n_heads, int n_c) {
   p.n_heads = n_heads;
   p.n_c = n_c;
   p.N = n_heads * (int64_t)n_c;
-  p.tiles_per_head = (n_c + TILE - 1) / TILE;
+  p.tiles_per_head = (int)(((int64_t)n_c + TILE - 1) / TILE);  // n_c may be INT_MAX
   p.n_tiles = n_heads * p.tiles_per_head;
   p.total_bytes = align256((BINS0 + BINS1) * sizeof(uint32_t)) + align256(JBINS * sizeof(uint32_t)) +
                   align256(sizeof(SelState)) + 2 * align256((size_t)p.n_tiles * sizeof(uint32_t)) +

@@ -47,7 +47,7 @@ int main() {
     }
 
   // workspace queries: zero for bad sizes, no overflow for huge ones
-  const int sizes[] = {-1, 0, 1, 64, 128, 256, 2064, 131072, 1 << 24, 1 << 30};
+  const int sizes[] = {-1, 0, 1, 64, 128, 256, 2064, 131072, 1 << 24, 1 << 30, 2147483647};
   for (int H : sizes)
     for (int n : sizes) {
       (void)kvz_score_chunk_workspace(KVZ_BF16, H, 4, n, 128, n);
@@ -94,6 +94,18 @@ int main() {
   expect(kvz_select_tokens(Af, 4, 10, 3, Am, Ao, Am, A, 8, nullptr), WS, "tokens ws");
   expect(kvz_head_scores(nullptr, 4, 10, Af, nullptr), INV, "head_scores S");
   expect(kvz_token_scores(Af, 4, 0, Af, nullptr), INV, "token_scores n_c");
+
+  // launch-size limits (32-bit work-item counts, int row indices)
+  expect(kvz_score_chunk(KVZ_BF16, 4096, 1, 128, 64, 0, 1 << 20, A, A, A, 0.1f, Af, A, big, nullptr), INV, "score rows limit");
+  expect(kvz_score_chunk(KVZ_BF16, 4096, 1, 64, 1 << 24, 0, 16, A, A, A, 0.1f, Af, A, big, nullptr), INV, "score pass-2 grid");
+  expect(kvz_score_chunk_attn(KVZ_BF16, 4096, 1, 256, 64, 0, 1 << 17, A, A, A, A, A, 0.1f, Af, Af, A, big, nullptr), INV, "attn merge grid");
+  expect(kvz_score_chunk_noalloc(KVZ_BF16, 4096, 1, 128, 64, 0, 1 << 20, A, A, A, 0.1f, Af, nullptr), INV, "noalloc rows limit");
+  expect(kvz_select_threshold(Af, int64_t(1) << 24, 64, 5, Am, Ao, Af, A, big, nullptr), INV, "select tiles");
+  expect(kvz_head_scores(Af, int64_t(1) << 22, 1, Af, nullptr), INV, "head_scores heads");
+  expect(kvz_select_heads(Af, int64_t(1) << 22, 1, 1, 0, 0, Am, Ao, Am, A, big, nullptr), INV, "heads count");
+  expect(kvz_decode_packed(KVZ_BF16, 16, 1, 64, 2147483647, A, A, A, Ao, 0.1f, Af, A, big, nullptr), INV, "decode segments");
+  expect(kvz_decode_packed(KVZ_BF16, 15, 1, 64, 2147483647, A, A, A, Ao, 0.1f, Af, A, 8, nullptr), WS, "decode max_len INT_MAX");
+  expect(kvz_decode_packed(KVZ_BF16, int64_t(1) << 21, 8, 256, 1, A, A, A, Ao, 0.1f, Af, A, big, nullptr), INV, "decode merge grid");
 
   // compaction and decode
   int32_t* Ai = static_cast<int32_t*>(A);

@@ -2,8 +2,8 @@
 status strings, the timer's host paths) under AddressSanitizer and
 UndefinedBehaviorSanitizer.  The library's sources are compiled with both
 sanitizers on their host side (device code as usual), linked to
-tests/abi_sanitize.cpp, and run; no GPU is needed because no call in the
-driver gets past validation."""
+tests/abi_sanitize.cpp, and run; no GPU is needed because no call in that
+test program gets past validation."""
 import os
 import shutil
 import subprocess
