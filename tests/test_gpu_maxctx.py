@@ -1,7 +1,8 @@
-"""The longest context one scoring call takes at d = 128: n_c = 8,388,607 keys
-(one head's keys just under 2 GiB in bf16, the range of the buffer loads
-that stage them), ragged in its last 32-key tile, against the oracle on the
-whole problem.
+"""The longest context one scoring call takes: one head's keys just under
+2 GiB in bf16 (the range of the buffer loads that stage them), n_c =
+16,777,215 / 8,388,607 / 4,194,303 keys at d = 64 / 128 / 256, ragged in
+the last 32-key tile, against the oracle on the whole problem (bf16 at each
+d, fp32 at d = 128).
 
 Query rows are zero except a few planted ones (a multiple of one key), so
 the scores span the uniform floor 1/(n_c + i + 1) of the zero rows and the
@@ -27,22 +28,26 @@ pytestmark = pytest.mark.gpu
 
 torch = pytest.importorskip("torch")
 
-N_C, D, N_IN, N_PROMPT = 8_388_607, 128, 64, 16
-ALPHA = 2.3
-# (row i, target) with one query head: targets are context keys ("c", j) or
-# chunk keys ("in", m), m <= i
-PLANTED = [(63, ("c", N_C - 1)), (1, ("c", 0)), (32, ("c", 1 << 22)), (40, ("in", 20)),
-           (50, ("c", N_C - 33))]
+N_IN, N_PROMPT = 64, 16
+ALPHA = 2.5
+N_C_MAX = {64: 16_777_215, 128: 8_388_607, 256: 4_194_303}  # n_c * d * 2 < 2^31
 
 
-def _device_inputs(dtype):
+def _planted(n_c):
+    """(row i, target) with one query head: targets are context keys
+    ("c", j) or chunk keys ("in", m), m <= i."""
+    return [(63, ("c", n_c - 1)), (1, ("c", 0)), (32, ("c", n_c // 2)), (40, ("in", 20)),
+            (50, ("c", n_c - 33))]
+
+
+def _device_inputs(dtype, N_C, D):
     gen = torch.Generator(device="cuda")
     gen.manual_seed(20261205)
     tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
     r = lambda *s: torch.randn(*s, generator=gen, device="cuda", dtype=torch.float32).to(tdt)
     kc, vc, kin, vin = r(1, N_C, D), r(1, N_C, D), r(1, N_IN, D), r(1, N_IN, D)
     q = torch.zeros(1, 1, N_IN, D, dtype=tdt, device="cuda")
-    for i, (kind, t) in PLANTED:
+    for i, (kind, t) in _planted(N_C):
         q[0, 0, i] = (ALPHA * (kc[0, t] if kind == "c" else kin[0, t]).float()).to(tdt)
     torch.cuda.synchronize()
     return q, kc, kin, vc, vin
@@ -52,9 +57,10 @@ def _f64(x, dtype):
     return ras.to_f64(bits_of(x) if dtype == "bf16" else x.cpu().numpy(), dtype)
 
 
-@pytest.mark.parametrize("dtype", ["bf16", "f32"])
-def test_scores_and_output_at_the_context_limit(dtype):
-    q, kc, kin, vc, vin = _device_inputs(dtype)
+@pytest.mark.parametrize("dtype,D", [("bf16", 64), ("bf16", 128), ("bf16", 256), ("f32", 128)])
+def test_scores_and_output_at_the_context_limit(dtype, D):
+    N_C = N_C_MAX[D]
+    q, kc, kin, vc, vin = _device_inputs(dtype, N_C, D)
     scale = 1.0 / math.sqrt(D)
     S1 = torch.zeros(1, N_C, dtype=torch.float32, device="cuda")
     kvz.kvz_score_chunk(q, kc, kin, S1, N_PROMPT, scale)

@@ -186,6 +186,20 @@ def test_degenerate_shapes(case):
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_most_heads_in_one_call(dtype):
+    """4096 KV heads in one call (the most it takes), checked on sampled
+    heads spread over the grid (first, last, and around the XCD boundaries
+    of the head-major workgroup order)."""
+    wl = Workload("heads4096", 17, 1, 4096, 2, 64, 100, 40, 8, 0.3, dtype=dtype)
+    gen = HostGen(wl)
+    got = gpu_layer_scores(gen, 0)
+    heads = [0, 1, 511, 512, 2047, 2048, 3583, 4095]
+    ref = oracle_layer_scores(gen, 0, heads)
+    tol = dict(atol=1e-6, rtol=1e-4) if dtype == "f32" else {}
+    assert_scores_close(got[heads], ref, what=f"4096 heads {dtype}", **tol)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
 def test_resume_from_saved_scores_is_bitwise_identical(dtype):
     """Scoring can stop after any chunk and resume from a host copy of S: the
     result equals the uninterrupted run bit for bit (S is the whole state)."""

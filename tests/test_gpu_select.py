@@ -122,6 +122,36 @@ def test_select_at_the_size_limit():
         assert np.array_equal(got, want), f"mask differs at {f0 + np.nonzero(got != want)[0][:5]}"
 
 
+def test_compact_at_the_mask_index_limit():
+    """Compaction of the last 4 of 16384 heads of 131071 positions: the mask
+    rows it reads start just below 2^31 bytes into the mask.  Earlier heads
+    keep nothing (zero mask rows, zero offsets), so the packed output is only
+    the 4 heads' rows; bit-exact against the oracle's compaction of them."""
+    n_heads, n_c, d, hb, hc = 16384, 131071, 128, 16380, 4
+    assert (hb + hc) * n_c < 1 << 31 <= (hb + hc) * n_c + n_c * 8
+    rng = np.random.default_rng(31)
+    sub = (rng.random((hc, n_c)) < 0.3).astype(np.uint8)
+    sub[1] = 0                                       # an empty head
+    sub[2, -1] = 1                                   # the very last position
+    mask = torch.zeros(n_heads * n_c, dtype=torch.uint8, device="cuda")
+    mask[hb * n_c:].copy_(torch.from_numpy(sub.reshape(-1)))
+    counts = sub.sum(axis=1, dtype=np.int64)
+    offs = np.zeros(hb + hc + 1, np.int64)
+    offs[hb + 1:] = np.cumsum(counts)
+    kc = rng.integers(0, 1 << 16, (hc, n_c, d), dtype=np.uint16)
+    vc = rng.integers(0, 1 << 16, (hc, n_c, d), dtype=np.uint16)
+    K = int(offs[-1])
+    ko = torch.empty(K, d, dtype=torch.bfloat16, device="cuda")
+    vo = torch.empty_like(ko)
+    idx = torch.empty(K, dtype=torch.int32, device="cuda")
+    kvz.kvz_compact(to_dev(kc, "bf16"), to_dev(vc, "bf16"), mask, torch.from_numpy(offs).cuda(),
+                    ko, vo, idx, head_begin=hb)
+    torch.cuda.synchronize()
+    rko, rvo, ridx = ras.compact(kc, vc, sub.reshape(-1), offs[hb:] - offs[hb])
+    assert np.array_equal(bits_of(ko), rko) and np.array_equal(bits_of(vo), rvo)
+    assert np.array_equal(idx.cpu().numpy(), ridx)
+
+
 def _compact_case(wl, dtype, K_ratio, per_layer, mask_offset=0):
     rng = np.random.default_rng(wl.seed)
     n_heads, n_c, d = wl.n_heads, wl.n_ctx, wl.head_dim
