@@ -133,7 +133,7 @@ kvz_status kvz_score_chunk_ex(kvz_dtype dt, kvz_aggregate agg, int H, int G, int
   clear_error();
   const hipError_t e = score_launch(dt, agg, p, q, k_ctx, k_in, scale, S, ws,
                                     reinterpret_cast<hipStream_t>(stream));
-  return e == hipSuccess ? KVZ_OK : KVZ_ERR_HIP;
+  return KVZ_RESULT(e, debug_word_score, reinterpret_cast<hipStream_t>(stream));
 }
 
 kvz_status kvz_score_chunk(kvz_dtype dt, int H, int G, int d, int n_c, int n_prompt, int n_in,
@@ -180,7 +180,7 @@ kvz_status kvz_score_chunk_attn(kvz_dtype dt, int H, int G, int d, int n_c, int 
   if (dt == KVZ_F32) e = score_launch(dt, KVZ_AGG_MAX, p, q, k_ctx, k_in, scale, S, ws, st);
   if (e == hipSuccess)
     e = attn_launch(dt, p, a, q, k_ctx, k_in, v_ctx, v_in, scale, S, O, ws, st);
-  return e == hipSuccess ? KVZ_OK : KVZ_ERR_HIP;
+  return KVZ_RESULT(e, debug_word_score, st);
 }
 
 // head maxima: one 1024-thread workgroup per head, so that the launch's
@@ -231,7 +231,7 @@ kvz_status kvz_select_heads(const float* S, int64_t n_heads, int n_c, int64_t K_
   const hipError_t e = select_heads_launch(S, n_heads, n_c, K_heads, n_sink, n_recent, mask,
                                            head_offsets, head_keep, ws,
                                            reinterpret_cast<hipStream_t>(stream));
-  return e == hipSuccess ? KVZ_OK : KVZ_ERR_HIP;
+  return KVZ_RESULT(e, debug_word_select, reinterpret_cast<hipStream_t>(stream));
 }
 
 size_t kvz_select_tokens_workspace(int64_t n_heads, int n_c) {
@@ -253,7 +253,7 @@ kvz_status kvz_select_tokens(const float* S, int64_t n_heads, int n_c, int64_t K
   clear_error();
   const hipError_t e = select_tokens_launch(S, n_heads, n_c, K_tokens, mask, head_offsets,
                                             token_keep, ws, reinterpret_cast<hipStream_t>(stream));
-  return e == hipSuccess ? KVZ_OK : KVZ_ERR_HIP;
+  return KVZ_RESULT(e, debug_word_select, reinterpret_cast<hipStream_t>(stream));
 }
 
 int64_t kvz_keep_count(int64_t N, double r) {
@@ -293,7 +293,7 @@ kvz_status kvz_select_threshold(const float* S, int64_t n_heads, int n_c, int64_
   clear_error();
   const hipError_t e = select_launch(p, S, K, mask, head_offsets, tau_out, ws,
                                      reinterpret_cast<hipStream_t>(stream));
-  return e == hipSuccess ? KVZ_OK : KVZ_ERR_HIP;
+  return KVZ_RESULT(e, debug_word_select, reinterpret_cast<hipStream_t>(stream));
 }
 
 size_t kvz_compact_workspace(int64_t head_count, int n_c) {
@@ -326,7 +326,7 @@ kvz_status kvz_compact(kvz_dtype dt, int d, int n_c, int64_t head_begin, int64_t
   const hipError_t e = compact_launch(p, row_bytes, head_begin, k_ctx, v_ctx, mask, head_offsets,
                                       k_out, v_out, idx_out, ws,
                                       reinterpret_cast<hipStream_t>(stream));
-  return e == hipSuccess ? KVZ_OK : KVZ_ERR_HIP;
+  return KVZ_RESULT(e, debug_word_compact, reinterpret_cast<hipStream_t>(stream));
 }
 
 // Both decode launches stay below 2^32 work-items: one 256-thread workgroup
@@ -363,7 +363,7 @@ kvz_status kvz_decode_packed(kvz_dtype dt, int64_t n_heads, int G, int d, int ma
   clear_error();
   const hipError_t e = decode_launch(dt, p, q, k_rows, v_rows, head_offsets, scale, out, ws,
                                      reinterpret_cast<hipStream_t>(stream));
-  return e == hipSuccess ? KVZ_OK : KVZ_ERR_HIP;
+  return KVZ_RESULT(e, debug_word_decode, reinterpret_cast<hipStream_t>(stream));
 }
 
 kvz_status kvz_prof_enable(int on, int max_launches) {

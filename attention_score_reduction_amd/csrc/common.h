@@ -42,6 +42,44 @@ __device__ __forceinline__ bf16x8 as_bf16x8(uint4 u) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Debug builds (-DKVZ_DEBUG, libkvz_debug.so).  Kernels check conditions
+// their inputs must meet and invariants of their own results; a failed check
+// sets a bit in a device word of its source file (KVZ_DCHECK) instead of
+// trapping, and never changes what a kernel reads or writes.  The call that
+// launched the kernels synchronises its stream, takes and clears the word
+// (debug_word_<file>), and returns KVZ_ERR_INVALID_ARG when a bit was set.
+// Release builds compile every check away.  The words are per device and
+// shared by all calls on it: debug builds are meant for one caller thread.
+#ifdef KVZ_DEBUG
+#define KVZ_DEBUG_WORD(fn)                                                            \
+  static __device__ unsigned int kvz_dbg_word;                                        \
+  unsigned int fn(hipStream_t st) {                                                   \
+    unsigned int v = 0, z = 0;                                                        \
+    if (hipStreamSynchronize(st) != hipSuccess) return ~0u;                           \
+    if (hipMemcpyFromSymbol(&v, HIP_SYMBOL(kvz_dbg_word), sizeof v) != hipSuccess)    \
+      return ~0u;                                                                     \
+    if (v && hipMemcpyToSymbol(HIP_SYMBOL(kvz_dbg_word), &z, sizeof z) != hipSuccess) \
+      return ~0u;                                                                     \
+    return v;                                                                         \
+  }
+#define KVZ_DCHECK(cond, bit)                          \
+  do {                                                 \
+    if (!(cond)) atomicOr(&kvz_dbg_word, (bit));       \
+  } while (0)
+unsigned int debug_word_score(hipStream_t st);
+unsigned int debug_word_select(hipStream_t st);
+unsigned int debug_word_compact(hipStream_t st);
+unsigned int debug_word_decode(hipStream_t st);
+#define KVZ_RESULT(e, word, st) \
+  ((e) != hipSuccess ? KVZ_ERR_HIP : ((word)(st) != 0u ? KVZ_ERR_INVALID_ARG : KVZ_OK))
+#else
+#define KVZ_RESULT(e, word, st) ((e) == hipSuccess ? KVZ_OK : KVZ_ERR_HIP)
+#define KVZ_DEBUG_WORD(fn)
+#define KVZ_DCHECK(cond, bit) \
+  do {                        \
+  } while (0)
+#endif
+
 // Compensated (Kahan) accumulation: sum += term, with the rounding error of
 // each step carried in comp, so that terms far below the running sum still
 // count.  Contraction is off: every step must round on its own.

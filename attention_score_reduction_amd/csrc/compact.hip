@@ -18,6 +18,8 @@
 
 namespace kvz {
 
+KVZ_DEBUG_WORD(debug_word_compact)
+
 namespace {
 
 // Measured on the 30%-kept 128K cache (10.4 GB moved): tiles of 4096, 1024,
@@ -87,6 +89,14 @@ __global__ __launch_bounds__(TPB) void cmp_offsets(const uint8_t* __restrict__ m
   }
   if (lane == 63) wtot[w] = incl;
   __syncthreads();
+#ifdef KVZ_DEBUG
+  if (t == 0) {  // the head's kept rows must fill its range of the packed output
+    uint32_t kept = 0;
+    for (int ww = 0; ww < TPB / 64; ++ww) kept += wtot[ww];
+    KVZ_DCHECK((int64_t)kept == head_offsets[head_begin + hh + 1] - head_offsets[head_begin + hh],
+               1u);
+  }
+#endif
   uint32_t before = incl - mine;
   for (int ww = 0; ww < w; ++ww) before += wtot[ww];
   int64_t run = head_offsets[head_begin + hh] + before;

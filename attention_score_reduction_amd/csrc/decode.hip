@@ -21,6 +21,8 @@
 
 namespace kvz {
 
+KVZ_DEBUG_WORD(debug_word_decode)
+
 namespace {
 
 constexpr int TPB = 256;
@@ -107,6 +109,8 @@ __global__ __launch_bounds__(TPB) void decode_split(const T* __restrict__ q,
   const int64_t h = blockIdx.x / n_seg;
   const int seg = blockIdx.x - (int)h * n_seg;
   const int64_t a = offs[h], b = offs[h + 1];
+  // offsets non-decreasing, no head longer than max_len (rows past it are not read)
+  KVZ_DCHECK(b >= a && b - a <= (int64_t)n_seg * seg_rows, 1u);
   const int64_t r0 = a + (int64_t)seg * seg_rows;
   if (r0 >= b) return;  // segment past this head's rows (decode_combine skips it)
   const int64_t r1 = min(b, r0 + seg_rows);

@@ -80,5 +80,5 @@ extern "C" kvz_status kvz_score_chunk_noalloc(kvz_dtype dt, int H, int G, int d,
   (void)hipGetLastError();
   e = score_launch(dt, KVZ_AGG_MAX, p, q, k_ctx, k_in, scale, S, ws,
                    reinterpret_cast<hipStream_t>(stream));
-  return e == hipSuccess ? KVZ_OK : KVZ_ERR_HIP;
+  return KVZ_RESULT(e, debug_word_score, reinterpret_cast<hipStream_t>(stream));
 }

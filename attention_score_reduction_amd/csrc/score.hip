@@ -32,6 +32,8 @@
 
 namespace kvz {
 
+KVZ_DEBUG_WORD(debug_word_score)
+
 namespace {
 
 constexpr int KT = 32;          // keys per pass-1 tile
@@ -500,6 +502,7 @@ __global__ __launch_bounds__(256) void score_combine(const float2* __restrict__ 
     const float2 v = p[(size_t)s * R_pad];
     kahan_add(L, c, v.y * exp2f(v.x - M));
   }
+  KVZ_DCHECK(isfinite(M + log2f(L)), 1u);  // NaN or inf in q or the keys
   lse2[idx] = (M + log2f(L)) * mul;
 }
 
@@ -755,6 +758,7 @@ __global__ __launch_bounds__(64) void score_pass1_f32(const float* __restrict__ 
       m = mn;
     }
   }
+  KVZ_DCHECK(r >= R || isfinite(m + log2f(l)), 1u);  // NaN or inf in q or the keys
   if (r < R_pad) lse2[(size_t)h * R_pad + r] = (r < R) ? m + log2f(l) : INFINITY;
 }
 

@@ -37,6 +37,8 @@
 
 namespace kvz {
 
+KVZ_DEBUG_WORD(debug_word_select)
+
 namespace {
 
 // radix digits of the 32-bit key: bits 31..20 (first pass), 19..10 and 9..0
@@ -106,6 +108,7 @@ __global__ __launch_bounds__(TPB) void sel_hist0(const float* __restrict__ S, lo
 #pragma unroll
     for (int u = 0; u < HU; ++u) {
       if (i0 + (long long)u * TPB < n4) {
+        KVZ_DCHECK(!isnan(v[u].x) && !isnan(v[u].y) && !isnan(v[u].z) && !isnan(v[u].w), 1u);
         atomicAdd(&h[(fkey(v[u].x) >> B0_SHIFT) * HR + rep], 1u);
         atomicAdd(&h[(fkey(v[u].y) >> B0_SHIFT) * HR + rep], 1u);
         atomicAdd(&h[(fkey(v[u].z) >> B0_SHIFT) * HR + rep], 1u);
@@ -114,8 +117,10 @@ __global__ __launch_bounds__(TPB) void sel_hist0(const float* __restrict__ S, lo
     }
   }
   if (blockIdx.x == 0)
-    for (long long i = (n4 << 2) + threadIdx.x; i < N; i += TPB)
+    for (long long i = (n4 << 2) + threadIdx.x; i < N; i += TPB) {
+      KVZ_DCHECK(!isnan(S[i]), 1u);
       atomicAdd(&h[(fkey(S[i]) >> B0_SHIFT) * HR + rep], 1u);
+    }
   __syncthreads();
   for (int b = threadIdx.x; b < BINS0; b += TPB) {
     uint32_t c = 0;
@@ -546,6 +551,7 @@ __global__ __launch_bounds__(SCAN_T) void sel_heads(const SelState* __restrict__
     hrun += head_sum(h);
   }
   if (t == 0) {
+    KVZ_DCHECK((long long)total == st->krem[0], 2u);  // exactly K kept
     head_offsets[n_heads] = total;
     *tau_out = key_to_float(st->tau);
   }

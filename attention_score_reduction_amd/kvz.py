@@ -12,6 +12,7 @@ import os
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libkvz.so")
+DEBUG_LIB_PATH = os.path.join(HERE, "libkvz_debug.so")
 
 KVZ_OK, KVZ_ERR_INVALID_ARG, KVZ_ERR_UNSUPPORTED, KVZ_ERR_WORKSPACE, KVZ_ERR_HIP = range(5)
 KVZ_BF16, KVZ_F32 = 0, 1
@@ -29,7 +30,8 @@ SYMBOLS = (
     "kvz_decode_packed", "kvz_prof_enable", "kvz_prof_read",
 )
 
-_lib = None
+_libs = {}
+_use_debug = False
 
 
 class KvzError(RuntimeError):
@@ -38,29 +40,42 @@ class KvzError(RuntimeError):
         super().__init__(f"{where}: {kvz_status_string(status)} (status {status})")
 
 
+def use_debug_library(on: bool = True):
+    """Route every binding of this module to libkvz_debug.so (the checked
+    build: a failed kernel-side check returns KVZ_ERR_INVALID_ARG) or, with
+    on=False, back to libkvz.so."""
+    global _use_debug
+    _use_debug = bool(on)
+
+
 def lib():
-    """Load libkvz.so (once) and declare its signatures."""
-    global _lib
-    if _lib is not None:
-        return _lib
+    """The library the bindings call (libkvz.so, or libkvz_debug.so after
+    use_debug_library()), loaded once, its signatures declared."""
+    key = "debug" if _use_debug else "release"
+    if key not in _libs:
+        _libs[key] = _open(DEBUG_LIB_PATH if _use_debug else LIB_PATH, _use_debug)
+    return _libs[key]
+
+
+def _open(path, debug):
     # torch ships its own HIP runtime under the same soname (libamdhip64.so.7);
     # loading torch first makes libkvz bind to that runtime, so the streams
     # and device pointers torch hands over belong to the runtime that
     # launches the kernels.  Opened the other way round, the process would
     # hold two HIP runtimes and every launch on a torch stream would fail.
     import torch  # noqa: F401
-    if not os.path.exists(LIB_PATH):
+    if not os.path.exists(path):
         raise RuntimeError(
-            f"{LIB_PATH} is missing: build it with `python -c 'import __graft_entry__ as g; g.build()'`"
+            f"{path} is missing: build it with `python -c 'import __graft_entry__ as g; g.build()'`"
             " (the HIP library is required; there is no CPU fallback)")
-    L = ctypes.CDLL(LIB_PATH)
+    L = ctypes.CDLL(path)
     L.kvz_build_id.argtypes = []
     L.kvz_build_id.restype = ctypes.c_char_p
     from .build import source_digest
-    built, want = L.kvz_build_id().decode(), source_digest()
+    built, want = L.kvz_build_id().decode(), source_digest(debug)
     if built != want:
         raise RuntimeError(
-            f"{LIB_PATH} was built from other sources (build id {built[:16]}) than the ones in "
+            f"{path} was built from other sources (build id {built[:16]}) than the ones in "
             f"this checkout (digest {want[:16]}): rebuild it with "
             "`python -c 'import __graft_entry__ as g; g.build()'`")
     c_int, c_i64, c_sz, c_f, c_d, c_p = (ctypes.c_int, ctypes.c_int64, ctypes.c_size_t,
@@ -116,7 +131,6 @@ def lib():
     L.kvz_prof_enable.restype = c_int
     L.kvz_prof_read.argtypes = [ctypes.c_char_p, ctypes.POINTER(c_i64), ctypes.POINTER(c_d)]
     L.kvz_prof_read.restype = c_int
-    _lib = L
     return L
 
 

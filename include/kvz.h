@@ -37,6 +37,15 @@
  *   - The library keeps no state between calls except the optional profiler
  *     below; calls on different streams may run concurrently if their
  *     buffers and workspaces are disjoint.
+ *   - libkvz_debug.so, the same sources built with KVZ_DEBUG, exports the
+ *     same calls.  Its kernels also check conditions the documentation puts
+ *     on device-side data (no NaN or inf in scores, queries and keys; head
+ *     offsets that match the mask they come with; no packed head longer
+ *     than max_len) and invariants of their own results (exactly K kept).
+ *     Where the release library returns a silent result for such input, the
+ *     debug library synchronises the stream after the call and returns
+ *     KVZ_ERR_INVALID_ARG.  Its checks share one flag per device: use it
+ *     from one thread.
  */
 #ifndef KVZ_H_
 #define KVZ_H_

@@ -26,10 +26,29 @@ def test_library_exports_every_declared_symbol():
         assert hasattr(L, n), n
 
 
-def test_nm_shows_exports():
-    out = os.popen(f"nm -D --defined-only {kvz.LIB_PATH}").read()
+@pytest.mark.parametrize("path", [kvz.LIB_PATH, kvz.DEBUG_LIB_PATH])
+def test_nm_shows_exports(path):
+    out = os.popen(f"nm -D --defined-only {path}").read()
     for n in _declared():
         assert re.search(rf"\bT {n}\b", out), n
+
+
+def test_debug_library_loads_and_validates_like_release():
+    """libkvz_debug.so carries its own build id (the sources plus its debug
+    flag) and rejects bad arguments exactly as libkvz.so does."""
+    R = kvz.lib()
+    try:
+        kvz.use_debug_library(True)
+        D = kvz.lib()
+        for n in _declared():
+            assert hasattr(D, n), n
+        assert D.kvz_build_id() != R.kvz_build_id()
+        assert D.kvz_score_chunk(0, 0, 4, 128, 100, 4, 20, FAKE, FAKE, FAKE, 0.1, FAKE, FAKE,
+                                 1 << 30, None) == kvz.KVZ_ERR_INVALID_ARG
+        assert D.kvz_decode_packed(0, 4, 9, 128, 100, FAKE, FAKE, FAKE, FAKE, 0.1, FAKE, FAKE,
+                                   1 << 30, None) == kvz.KVZ_ERR_UNSUPPORTED
+    finally:
+        kvz.use_debug_library(False)
 
 
 @pytest.mark.parametrize("N,r,K", [(512, 0.3, 154), (2097152, 0.3, 629146), (33554432, 0.3, 10066330),
