@@ -1,7 +1,8 @@
 """kvz_score_chunk_noalloc (fixed device scratch, no allocation) against
-kvz_score_chunk (caller workspace) through the C ABI: two calls in a row, the
-second with a smaller problem, each bit-identical to the workspace call (the
-same kernels and launch plan run on the same inputs)."""
+kvz_score_chunk (caller workspace) through the C ABI: calls in a row, each
+with a smaller problem than the one before (the first fills 89% of the
+16 MiB scratch), each bit-identical to the workspace call (the same kernels
+and launch plan run on the same inputs)."""
 import math
 
 import numpy as np
@@ -34,10 +35,15 @@ def _case(wl, chunk_ids):
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 def test_noalloc_matches_workspace_call_twice_shrinking(dtype):
+    # 32 KV heads x 8 query heads x 2064 rows: the bf16 plan needs 14.9 MB
+    fill = Workload("na_fill", 53, 1, 32, 8, 128, 2048, 2048, 16, 0.3, dtype=dtype)
+    need = kvz.kvz_score_chunk_workspace(kvz.KVZ_BF16 if dtype == "bf16" else kvz.KVZ_F32,
+                                         32, 8, 2064, 128, 2048)
+    assert need <= kvz.NOALLOC_SCRATCH_BYTES
     big = Workload("na_big", 51, 1, 4, 4, 128, 6000, 1500, 16, 0.3, dtype=dtype,
                    key_lognormal_sigma=0.5, sink=True)
     small = Workload("na_small", 52, 1, 2, 2, 64, 900, 300, 8, 0.3, dtype=dtype, sink=True)
-    for wl, ids in ((big, [0, 3]), (small, [0, 2])):
+    for wl, ids in ((fill, [0]), (big, [0, 3]), (small, [0, 2])):
         a, b = _case(wl, ids)
         assert np.array_equal(a, b), f"{wl.name}: noalloc scores differ from the workspace call"
         assert np.all(a > 0) and np.all(a <= 1)
