@@ -47,3 +47,42 @@ def test_noalloc_matches_workspace_call_twice_shrinking(dtype):
         a, b = _case(wl, ids)
         assert np.array_equal(a, b), f"{wl.name}: noalloc scores differ from the workspace call"
         assert np.all(a > 0) and np.all(a <= 1)
+
+
+def test_noalloc_calls_captured_in_a_graph():
+    """The callers this entry point is for include code under HIP graph
+    capture: three chunk calls captured into one graph (after a first,
+    uncaptured call has set up the scratch address), then replayed three
+    times with eager work between the replays; every replay gives the eager
+    result bit for bit (the scoring path records no memset node)."""
+    wl = Workload("na_graph", 54, 1, 4, 4, 128, 3000, 1000, 16, 0.3, key_lognormal_sigma=0.5)
+    gen = HostGen(wl)
+    kc, _ = gen.context(0)
+    kc_d = to_dev(kc, wl.dtype)
+    scale = 1 / math.sqrt(wl.head_dim)
+    chunks = []
+    for k in range(len(wl.chunks())):
+        q, kin = gen.chunk_inputs(0, k)
+        chunks.append((to_dev(q, wl.dtype), to_dev(kin, wl.dtype)))
+    S_eager = torch.zeros(wl.heads, wl.n_ctx, dtype=torch.float32, device="cuda")
+    for qd, kd in chunks:
+        kvz.kvz_score_chunk_noalloc(qd, kc_d, kd, S_eager, wl.n_prompt, scale)
+    torch.cuda.synchronize()
+    want = S_eager.cpu().numpy()
+
+    S = torch.zeros_like(S_eager)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(g, stream=side):
+            for qd, kd in chunks:
+                kvz.kvz_score_chunk_noalloc(qd, kc_d, kd, S, wl.n_prompt, scale, stream=side)
+    torch.cuda.current_stream().wait_stream(side)
+    for rep in range(3):
+        S.zero_()                                   # eager work between replays
+        noise = torch.randn(1 << 20, device="cuda")  # unrelated eager kernels
+        g.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(S.cpu().numpy(), want), f"replay {rep}"
+        del noise
